@@ -1,0 +1,182 @@
+"""Plain fp64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module. The product path (the HIP
+library and its Python binding) never calls it and shares no code with it.
+
+What is computed, and where the pages define it:
+
+* Forward: ``O = softmax(Q K^T * scale) V`` per (batch, query head).
+  Qiita FlashAttention tutorial (GeneLab_999), section 2.2 gives
+  ``softmax(QK^T / sqrt(d)) V``; the hysenlabs digest of the flash-attention
+  README ("FlashAttentionで見る出力と運用記録") gives the same with an explicit
+  ``softmax_scale``. The "standard attention" of tutorial section 4.1 (and
+  "基本アイデア" in the abeam.tech summary of the FlashAttention paper) is
+  computed literally: S is materialised, softmax is taken row by row, then
+  P V. FlashAttention is exact (abeam summary, "Softmax をブロック単位で正しく
+  計算する"): only the order of evaluation differs, so the plain definition is
+  the oracle for every tiled GPU result.
+* Causal masking keeps key j for query i iff j <= i + (Nk - Nq): the mask is
+  aligned to the bottom-right corner when the query and key lengths differ
+  (hysenlabs digest, "制約を切り分ける確認", v2.1 entry). With Nq == Nk this is
+  the usual j <= i.
+* MQA/GQA: Hq must be a multiple of Hkv (hysenlabs digest, "出力と運用記録").
+  Query head h reads key/value head h // (Hq // Hkv) (consecutive groups); the
+  pages only fix divisibility, so this grouping is a stated reading.
+* Logsumexp: the per-row normalisation statistic the forward keeps for the
+  recompute backward (abeam summary, "用語解説: Recomputation" and
+  "学習時の backward では再計算を使う") is taken to be the natural-log
+  logsumexp of the scaled, masked scores, ``LSE_i = log sum_j exp(S_ij)``.
+* Backward: the gradient of ``L = sum(O * dO)`` through the definition above,
+  i.e. the textbook softmax Jacobian (the pages say only that the backward
+  recomputes attention from the saved statistics):
+  ``dV = P^T dO``, ``dP = dO V^T``, ``D_i = sum_j P_ij dP_ij``,
+  ``dS = P * (dP - D)``, ``dQ = scale dS K``, ``dK = scale dS^T Q``;
+  dK and dV of a key/value head sum over the query heads of its group.
+* Decode with a KV cache (hysenlabs digest, ``flash_attn_with_kvcache``): one
+  query row per (sequence, head) attends keys 0 .. L_b - 1 of its cache
+  (with one query the bottom-right causal mask keeps every cached key).
+
+A fully masked row (only possible when causal and Nq > Nk) has O = 0 and
+LSE = -inf by convention.
+
+Inputs are numpy arrays of any float dtype; they are converted exactly to
+float64. Layouts: q, o, do, dq ``[B, Nq, Hq, d]``; k, v, dk, dv
+``[B, Nk, Hkv, d]``; lse ``[B, Hq, Nq]``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _check_heads(hq: int, hkv: int) -> int:
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"Hq={hq} must be a positive multiple of Hkv={hkv}")
+    return hq // hkv
+
+
+def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=None, nq=None):
+    """Scores, probabilities and logsumexp for one (batch, head).
+
+    q: [R, d] query rows, k: [Nk, d] (float64). ``rows`` gives the absolute
+    index of each query row among ``nq`` queries (default: all rows,
+    0 .. R-1 of R), which the causal mask needs. Returns (S, P, lse) where S
+    holds -inf at masked positions, P = softmax(S) row-wise (0 where
+    masked) and lse = log sum_j exp(S_ij) (-inf for a fully masked row).
+    """
+    nk = k.shape[0]
+    if rows is None:
+        rows = np.arange(q.shape[0])
+        nq = q.shape[0]
+    s = scale * (q @ k.T)
+    if causal:
+        keep = np.arange(nk)[None, :] <= np.asarray(rows)[:, None] + (nk - nq)
+        s = np.where(keep, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe)
+    l = e.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(empty, 0.0, e / np.where(empty, 1.0, l))
+        lse = np.where(empty[:, 0], -np.inf, m_safe[:, 0] + np.log(np.where(empty[:, 0], 1.0, l[:, 0])))
+    return s, p, lse
+
+
+def attn_fwd(q, k, v, scale: float, causal: bool):
+    """O = softmax(Q K^T * scale [+ causal mask]) V and the per-row logsumexp.
+
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]. Returns (o [B, Nq, Hq, d],
+    lse [B, Hq, Nq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, nq, hq, d = q.shape
+    _, nk, hkv, _ = k.shape
+    g = _check_heads(hq, hkv)
+    o = np.zeros((b_, nq, hq, d))
+    lse = np.zeros((b_, hq, nq))
+    for b in range(b_):
+        for h in range(hq):
+            kh = h // g
+            _, p, lse_bh = head_probs(q[b, :, h, :], k[b, :, kh, :], scale, causal)
+            o[b, :, h, :] = p @ v[b, :, kh, :]
+            lse[b, h, :] = lse_bh
+    return o, lse
+
+
+def attn_bwd(q, k, v, do, scale: float, causal: bool):
+    """Gradients of L = sum(O * dO) with respect to Q, K and V.
+
+    P is recomputed from Q and K (nothing from a forward pass is reused).
+    Returns (dq [B, Nq, Hq, d], dk [B, Nk, Hkv, d], dv [B, Nk, Hkv, d]) and
+    D = rowsum(P * dP) = rowsum(dO * O), shaped [B, Hq, Nq].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    b_, nq, hq, d = q.shape
+    _, nk, hkv, _ = k.shape
+    g = _check_heads(hq, hkv)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dd = np.zeros((b_, hq, nq))
+    for b in range(b_):
+        for h in range(hq):
+            kh = h // g
+            qh, kk, vv, doh = q[b, :, h, :], k[b, :, kh, :], v[b, :, kh, :], do[b, :, h, :]
+            _, p, _ = head_probs(qh, kk, scale, causal)
+            dv[b, :, kh, :] += p.T @ doh
+            dp = doh @ vv.T
+            drow = (p * dp).sum(axis=1, keepdims=True)
+            ds = p * (dp - drow)
+            dq[b, :, h, :] = scale * (ds @ kk)
+            dk[b, :, kh, :] += scale * (ds.T @ qh)
+            dd[b, h, :] = drow[:, 0]
+    return dq, dk, dv, dd
+
+
+def attn_decode(q, k_cache, v_cache, cache_seqlens, scale: float):
+    """One query row per (sequence, head) against that sequence's cache.
+
+    q: [B, Hq, d]; k_cache, v_cache: [B, Lmax, Hkv, d] (only rows
+    < cache_seqlens[b] are read); cache_seqlens: [B] ints in [1, Lmax].
+    Returns (o [B, Hq, d], lse [B, Hq]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    b_, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    g = _check_heads(hq, hkv)
+    o = np.zeros((b_, hq, d))
+    lse = np.zeros((b_, hq))
+    for b in range(b_):
+        n = int(cache_seqlens[b])
+        if n < 1 or n > k_cache.shape[1]:
+            raise ValueError(f"cache_seqlens[{b}]={n} outside [1, {k_cache.shape[1]}]")
+        kb = np.asarray(k_cache[b, :n], dtype=np.float64)
+        vb = np.asarray(v_cache[b, :n], dtype=np.float64)
+        for h in range(hq):
+            kh = h // g
+            _, p, lse_h = head_probs(q[b, h][None, :], kb[:, kh, :], scale, causal=False)
+            o[b, h] = (p @ vb[:, kh, :])[0]
+            lse[b, h] = lse_h[0]
+    return o, lse
+
+
+def attn_fwd_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
+    """Forward for selected query rows of one (batch, head) only.
+
+    Used to check large problems on sampled outputs: the cost is
+    O(len(rows) * Nk * d). Returns (o [len(rows), d], lse [len(rows)]).
+    """
+    hq, hkv = q.shape[2], k.shape[2]
+    kh = h // _check_heads(hq, hkv)
+    rows = np.asarray(rows)
+    qh = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    kk = np.asarray(k[b, :, kh, :], dtype=np.float64)
+    vv = np.asarray(v[b, :, kh, :], dtype=np.float64)
+    _, p, lse = head_probs(qh, kk, scale, causal, rows=rows, nq=q.shape[1])
+    return p @ vv, lse
