@@ -1,0 +1,9 @@
+"""Exact FlashAttention-style attention for MI355X (gfx950).
+
+The computation lives in libfa_mi355x.so (hand-written HIP kernels behind the
+C ABI of include/fa.h); this package only marshals torch tensors into it.
+"""
+from ._lib import FaError, load
+from .attention import fa_bwd, fa_decode_kvcache, fa_fwd
+
+__all__ = ["fa_fwd", "fa_bwd", "fa_decode_kvcache", "FaError", "load"]

@@ -1,0 +1,121 @@
+"""Torch-facing binding of the C ABI: argument marshalling only.
+
+Each function checks device, dtype, contiguity and shapes, allocates the
+outputs (and workspace) with torch, and passes raw device pointers plus the
+current HIP stream to the library. Every step of the computation runs in the
+library's HIP kernels.
+
+Layouts (as in include/fa.h): q, o, dout, dq ``[B, N, Hq, d]``;
+k, v, dk, dv ``[B, N, Hkv, d]``; lse ``[B, Hq, N]`` float32.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_DT = {torch.bfloat16: _lib.FA_BF16, torch.float32: _lib.FA_FP32}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_tensor(name, t, dtype=None, ndim=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """Attention forward. Returns (o, lse)."""
+    _check_tensor("q", q, ndim=4)
+    if q.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    _check_tensor("k", k, q.dtype, 4, q.device)
+    _check_tensor("v", v, q.dtype, 4, q.device)
+    B, N, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, q.dtype, 4, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_tensor("lse", lse, torch.float32, 3, q.device)
+    st = _lib.load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale,
+                            int(bool(causal)), _DT[q.dtype], _stream(q.device))
+    _lib.check(st)
+    return out, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False):
+    """Attention backward from the forward's O and LSE. Returns (dq, dk, dv)."""
+    _check_tensor("q", q, torch.bfloat16, 4)
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, torch.bfloat16, 4, dev)
+    _check_tensor("lse", lse, torch.float32, 3, dev)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if o.shape != q.shape or dout.shape != q.shape or k.shape != v.shape or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("inconsistent shapes for fa_bwd")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = _lib.load()
+    ws_bytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                    _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16, _stream(dev))
+    _lib.check(st)
+    return dq, dk, dv
+
+
+def fa_decode_kvcache(q, k_cache, v_cache, cache_seqlens, scale=None, causal=False, num_splits=0,
+                      out=None, lse=None, workspace=None):
+    """Decode one query token per sequence against a KV cache. Returns (o, lse).
+
+    q: [B, Hq, d]; k_cache, v_cache: [B, N, Hkv, d]; cache_seqlens: int32 [B].
+    """
+    _check_tensor("q", q, torch.bfloat16, 3)
+    dev = q.device
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
+    _check_tensor("cache_seqlens", cache_seqlens, torch.int32, 1, dev)
+    B, Hq, d = q.shape
+    _, N, Hkv, _ = k_cache.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d or cache_seqlens.shape[0] != B:
+        raise ValueError("inconsistent shapes for fa_decode_kvcache")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = _lib.load()
+    ws_bytes = lib.fa_decode_workspace_bytes(B, Hq, Hkv, N, d, int(num_splits))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    st = lib.fa_decode_kvcache(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse),
+                               _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, scale, int(bool(causal)),
+                               int(num_splits), _lib.FA_BF16, _stream(dev))
+    _lib.check(st)
+    return out, lse

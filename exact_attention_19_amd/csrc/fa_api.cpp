@@ -1,0 +1,169 @@
+// C ABI of the gfx950 attention library: argument validation, workspace
+// layout and kernel launches. Every check runs before any HIP call, so an
+// invalid call launches nothing. Declarations and argument documentation are
+// in include/fa.h.
+#include "../../include/fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fa_status ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+fa_status check_sizes(const char* fn, int B, int Hq, int Hkv, int N, int d, float scale) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%d Hq=%d Hkv=%d N=%d)", fn, B, Hq, Hkv, N);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(FA_ERR_INVALID_ARG, "%s: scale must be finite and positive", fn);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: head dim d=%d is not 64 or 128", fn, d);
+  // Element offsets are 64-bit, but one tensor must stay below 2^62 bytes.
+  const double elems = (double)B * N * Hq * d;
+  if (elems > 4.0e18) return fail(FA_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  return FA_OK;
+}
+
+fa_status check_ptr(const char* fn, const char* name, const void* p, size_t align) {
+  if (!p) return fail(FA_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned(p, align)) return fail(FA_ERR_INVALID_ARG, "%s: %s is not %zu-byte aligned", fn, name, align);
+  return FA_OK;
+}
+
+#define FA_TRY(expr)                 \
+  do {                               \
+    fa_status _st = (expr);          \
+    if (_st != FA_OK) return _st;    \
+  } while (0)
+
+fa_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t bwd_ws_bytes(int B, int Hq, int N) { return round_up((size_t)B * Hq * N * sizeof(float), 256); }
+
+void decode_ws_layout(int B, int Hq, int N, int d, int num_splits, int* chunk, int* nsplit, size_t* o_bytes,
+                      size_t* lse_bytes) {
+  fa::decode_split_plan(N, num_splits, chunk, nsplit);
+  *o_bytes = round_up((size_t)B * Hq * (size_t)(*nsplit) * d * sizeof(float), 256);
+  *lse_bytes = round_up((size_t)B * Hq * (size_t)(*nsplit) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_last_error(void) { return g_err; }
+
+const char* fa_version(void) { return "fa_mi355x 0.1 (gfx950)"; }
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                 int d, float scale, int causal, int dtype, void* stream) {
+  static const char* fn = "fa_fwd";
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16 && dtype != FA_FP32) return fail(FA_ERR_UNSUPPORTED, "%s: dtype %d not supported", fn, dtype);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k", k, 16));
+  FA_TRY(check_ptr(fn, "v", v, 16));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  FA_TRY(check_ptr(fn, "lse", lse, 4));
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal ? 1 : 0, dtype,
+                reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fn, fa::launch_fwd(a));
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  (void)Hkv;
+  (void)d;
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return bwd_ws_bytes(B, Hq, N);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                 int N, int d, float scale, int causal, int dtype, void* stream) {
+  static const char* fn = "fa_bwd";
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k", k, 16));
+  FA_TRY(check_ptr(fn, "v", v, 16));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  FA_TRY(check_ptr(fn, "dout", dout, 16));
+  FA_TRY(check_ptr(fn, "lse", lse, 4));
+  FA_TRY(check_ptr(fn, "dq", dq, 16));
+  FA_TRY(check_ptr(fn, "dk", dk, 16));
+  FA_TRY(check_ptr(fn, "dv", dv, 16));
+  const size_t need = bwd_ws_bytes(B, Hq, N);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
+                reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fn, fa::launch_bwd(a, static_cast<float*>(workspace)));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits) {
+  (void)Hkv;
+  if (B <= 0 || Hq <= 0 || N <= 0 || d <= 0 || num_splits < 0) return 0;
+  int chunk, nsplit;
+  size_t ob, lb;
+  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
+  return ob + lb;
+}
+
+fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* cache_seqlens,
+                            void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                            int N, int d, float scale, int causal, int num_splits, int dtype, void* stream) {
+  static const char* fn = "fa_decode_kvcache";
+  (void)causal;  // one query aligned to the bottom-right corner sees every cached key
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k_cache", k_cache, 16));
+  FA_TRY(check_ptr(fn, "v_cache", v_cache, 16));
+  FA_TRY(check_ptr(fn, "cache_seqlens", cache_seqlens, 4));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
+  int chunk, nsplit;
+  size_t ob, lb;
+  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
+  if (!workspace || workspace_bytes < ob + lb)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ob + lb,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ob);
+  fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
+                   reinterpret_cast<hipStream_t>(stream)};
+  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, chunk, nsplit));
+}
+
+}  // extern "C"

@@ -1,0 +1,490 @@
+// Backward attention kernels for gfx950 (MI355X).
+//
+// The backward pass recomputes the attention tiles from Q, K and the row
+// logsumexp saved by the forward instead of reading a stored S or P
+// (abeam.tech summary of the FlashAttention paper, "用語解説: Recomputation"
+// and "学習時の backward では再計算を使う"). With P_ij = exp(S_ij - LSE_i)
+// recomputed on chip, the gradients of L = sum(O * dO) are
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Three launches on one stream:
+//   1. preprocess: D = rowsum(dO * O) per (b, head, row), float32.
+//   2. dK/dV: one workgroup per (b, kv head, 128-key tile). Each wave keeps
+//      32 keys' K and V fragments and their dK^T, dV^T accumulators in
+//      registers and sweeps every query head of the GQA group and every
+//      64-row query tile that the causal mask leaves visible (S = Q K^T,
+//      dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS). dK and dV of a group
+//      are summed in registers, so nothing is accumulated in memory.
+//   3. dQ: one workgroup per (b, query head, 128-row query tile), shaped like
+//      the forward (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T).
+// No atomics: the result is bit-reproducible. dS is recomputed in both
+// kernels (seven tile products per tile pair instead of five).
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_c dO_ic O_ic
+template <int D>
+__global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __restrict__ o,
+                                                             const __bf16* __restrict__ dout,
+                                                             float* __restrict__ delta, int B, int Hq, int N) {
+  constexpr int LPT = D / 8;
+  const int64_t rows = (int64_t)B * N * Hq;
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = gt / LPT;
+  const int dl = (int)(gt % LPT);
+  const bool ok = r < rows;
+  const int64_t rr = ok ? r : 0;
+  const u32x4 a = *reinterpret_cast<const u32x4*>(o + rr * D + dl * 8);
+  const u32x4 g = *reinterpret_cast<const u32x4*>(dout + rr * D + dl * 8);
+  const float tot = row_group_sum<LPT>(dot8_bf16(a, g, 0.f));
+  if (ok && dl == 0) {
+    const int64_t per_b = (int64_t)N * Hq;
+    const int64_t b = rr / per_b;
+    const int64_t rem = rr - b * per_b;
+    const int64_t i = rem / Hq;
+    const int64_t h = rem - i * Hq;
+    delta[(b * Hq + h) * N + i] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV
+template <int D>
+struct DkdvSmem {
+  static constexpr int BQ = 64;
+  static constexpr int RS = D + 8;                 // padded row stride of Q and dO tiles
+  static constexpr int Q_OFF = 0;
+  static constexpr int DO_OFF = Q_OFF + BQ * RS;
+  static constexpr int QT_OFF = DO_OFF + BQ * RS;  // Q^T, 64 wide
+  static constexpr int DOT_OFF = QT_OFF + D * BQ;  // dO^T, 64 wide
+  static constexpr int STAGE_ELEMS = DOT_OFF + D * BQ;
+  static constexpr int STAGE_BYTES = STAGE_ELEMS * 2 + 2 * BQ * 4;  // + lse2, delta
+  static constexpr int BYTES = 2 * STAGE_BYTES;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
+    float scale_log2) {
+  using SM = DkdvSmem<D>;
+  constexpr int BQ = SM::BQ;
+  constexpr int BKV = 128;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int C8 = D / 8;
+  constexpr int GROUPS = (BQ / 4) * C8;  // 4-row x 8-dim staging groups per tile
+  constexpr int G_PER_T = (GROUPS + kBwdThreads - 1) / kBwdThreads;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BHK = B * Hkv;
+  const int bhk = blockIdx.x % BHK;
+  const int kt = blockIdx.x / BHK;  // low key tiles see the most query tiles: launched first
+  const int b = bhk / Hkv;
+  const int hk = bhk - b * Hkv;
+  const int G = Hq / Hkv;
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;
+  const bool wave_active = kw0 < N;
+
+  bf16x8 kf[DS], vf[DS];
+  {
+    const bool ok = my_key < N;
+    const int64_t off = ((int64_t)b * N + (ok ? my_key : 0)) * kv_rs + (int64_t)hk * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(k + off + 16 * s) : u32x4{0, 0, 0, 0});
+      vf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(v + off + 16 * s) : u32x4{0, 0, 0, 0});
+    }
+  }
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+  const int per_head = nqt - qt0;
+  const int n_iter = G * per_head;
+
+  u32x4 qreg[G_PER_T][4], dreg[G_PER_T][4];
+  float lreg = 0.f, dlreg = 0.f;
+
+  auto load_tile = [&](int it) {
+    const int hq = hk * G + it / per_head;
+    const int q0 = (qt0 + it % per_head) * BQ;
+    const __bf16* qb = q + (int64_t)b * N * q_rs + (int64_t)hq * D;
+    const __bf16* db = dout + (int64_t)b * N * q_rs + (int64_t)hq * D;
+#pragma unroll
+    for (int r = 0; r < G_PER_T; ++r) {
+      const int g = tid + r * kBwdThreads;
+      const int dc = g % C8, rg = g / C8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = q0 + rg * 4 + i;
+        const bool ok = g < GROUPS && row < N;
+        const int64_t off = (int64_t)row * q_rs + dc * 8;
+        qreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(qb + off) : u32x4{0, 0, 0, 0};
+        dreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(db + off) : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (tid < BQ) {
+      const int row = q0 + tid;
+      // Rows past N get LSE = +inf, so their recomputed probabilities are 0.
+      lreg = row < N ? lse[((int64_t)b * Hq + hq) * N + row] * kLog2e : __builtin_inff();
+    } else if (tid < 2 * BQ) {
+      const int row = q0 + tid - BQ;
+      dlreg = row < N ? delta[((int64_t)b * Hq + hq) * N + row] : 0.f;
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    __bf16* base = reinterpret_cast<__bf16*>(smem_raw + stage * SM::STAGE_BYTES);
+    float* fl = reinterpret_cast<float*>(smem_raw + stage * SM::STAGE_BYTES + SM::STAGE_ELEMS * 2);
+#pragma unroll
+    for (int r = 0; r < G_PER_T; ++r) {
+      const int g = tid + r * kBwdThreads;
+      if (g < GROUPS) {
+        const int dc = g % C8, rg = g / C8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<u32x4*>(base + SM::Q_OFF + (rg * 4 + i) * SM::RS + dc * 8) = qreg[r][i];
+          *reinterpret_cast<u32x4*>(base + SM::DO_OFF + (rg * 4 + i) * SM::RS + dc * 8) = dreg[r][i];
+        }
+        store_transposed_4x8(base + SM::QT_OFF, rg, dc, qreg[r]);
+        store_transposed_4x8(base + SM::DOT_OFF, rg, dc, dreg[r]);
+      }
+    }
+    if (tid < BQ) fl[tid] = lreg;
+    else if (tid < 2 * BQ) fl[tid] = dlreg;
+  };
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+
+  if (n_iter > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_iter; ++it) {
+    const int stage = it & 1;
+    const bool has_next = it + 1 < n_iter;
+    if (has_next) load_tile(it + 1);
+
+    const int q0 = (qt0 + it % per_head) * BQ;
+    const bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
+    if (!skip) {
+      const __bf16* base = reinterpret_cast<const __bf16*>(smem_raw + stage * SM::STAGE_BYTES);
+      const float* lse2 = reinterpret_cast<const float*>(smem_raw + stage * SM::STAGE_BYTES + SM::STAGE_ELEMS * 2);
+      const float* dlt = lse2 + BQ;
+      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N);
+      bf16x8 pb[4], dsb[4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        const __bf16* qrow = base + SM::Q_OFF + (qb * 32 + l32) * SM::RS + 8 * hh;
+        const __bf16* drow = base + SM::DO_OFF + (qb * 32 + l32) * SM::RS + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + 16 * s), kf[s], sacc);
+          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + 16 * s), vf[s], dpacc);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int qi = qb * 32 + 8 * j + 4 * hh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qi);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + qi);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = 4 * j + i;
+            float p = fast_exp2(sacc[e] * scale_log2 - l4[i]);
+            if (need_mask) {
+              const int query = q0 + qi + i;
+              const bool masked = (my_key >= N) || (CAUSAL && my_key > query);
+              p = masked ? 0.f : p;
+            }
+            const float ds = p * (dpacc[e] - d4[i]);
+            pb[qb * 2 + (e >> 3)][e & 7] = (__bf16)p;
+            dsb[qb * 2 + (e >> 3)][e & 7] = (__bf16)ds;
+          }
+        }
+      }
+#pragma unroll
+      for (int dbk = 0; dbk < DB; ++dbk) {
+        const int d = dbk * 32 + l32;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          dvacc[dbk] = mfma32(load_tr_operand(base + SM::DOT_OFF, d, st, hh), pb[st], dvacc[dbk]);
+          dkacc[dbk] = mfma32(load_tr_operand(base + SM::QT_OFF, d, st, hh), dsb[st], dkacc[dbk]);
+        }
+      }
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active || my_key >= N) return;
+  const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
+#pragma unroll
+  for (int dbk = 0; dbk < DB; ++dbk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = dbk * 32 + 8 * j + 4 * hh;
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dkacc[dbk][4 * j + 0] * scale, dkacc[dbk][4 * j + 1] * scale);
+      wk[1] = pack_bf16x2(dkacc[dbk][4 * j + 2] * scale, dkacc[dbk][4 * j + 3] * scale);
+      wv[0] = pack_bf16x2(dvacc[dbk][4 * j + 0], dvacc[dbk][4 * j + 1]);
+      wv[1] = pack_bf16x2(dvacc[dbk][4 * j + 2], dvacc[dbk][4 * j + 3]);
+      *reinterpret_cast<u32x2*>(dk + off + d) = wk;
+      *reinterpret_cast<u32x2*>(dv + off + d) = wv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ
+template <int D>
+struct DqSmem {
+  static constexpr int BN = 64;
+  static constexpr int RS = D + 8;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = K_OFF + BN * RS;
+  static constexpr int KT_OFF = V_OFF + BN * RS;  // K^T, 64 wide
+  static constexpr int STAGE_ELEMS = KT_OFF + D * BN;
+  static constexpr int BYTES = 2 * STAGE_ELEMS * 2;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles) {
+  using SM = DqSmem<D>;
+  constexpr int BN = SM::BN;
+  constexpr int BM = 128;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int C8 = D / 8;
+  constexpr int GROUPS = (BN / 4) * C8;
+  constexpr int G_PER_T = (GROUPS + kBwdThreads - 1) / kBwdThreads;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = B * Hq;
+  const int bh = blockIdx.x % BH;
+  const int rank = blockIdx.x / BH;
+  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+  const bool wave_active = qw0 < N;
+
+  bf16x8 qf[DS], dof[DS];
+  float my_lse2 = __builtin_inff(), my_dlt = 0.f;
+  {
+    const bool ok = my_q < N;
+    const int64_t off = ((int64_t)b * N + (ok ? my_q : 0)) * q_rs + (int64_t)hq * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(q + off + 16 * s) : u32x4{0, 0, 0, 0});
+      dof[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(dout + off + 16 * s) : u32x4{0, 0, 0, 0});
+    }
+    if (ok) {
+      my_lse2 = lse[((int64_t)b * Hq + hq) * N + my_q] * kLog2e;
+      my_dlt = delta[((int64_t)b * Hq + hq) * N + my_q];
+    }
+  }
+
+  int kv_end = N;
+  if (CAUSAL) kv_end = min(N, q0 + BM);
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const __bf16* kb = k + (int64_t)b * N * kv_rs + (int64_t)hk * D;
+  const __bf16* vb = v + (int64_t)b * N * kv_rs + (int64_t)hk * D;
+
+  u32x4 kreg[G_PER_T][4], vreg[G_PER_T][4];
+  auto load_tile = [&](int t) {
+    const int k0 = t * BN;
+#pragma unroll
+    for (int r = 0; r < G_PER_T; ++r) {
+      const int g = tid + r * kBwdThreads;
+      const int dc = g % C8, kg = g / C8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kg * 4 + i;
+        const bool ok = g < GROUPS && key < N;
+        const int64_t off = (int64_t)key * kv_rs + dc * 8;
+        kreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
+        vreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&](int stage) {
+    __bf16* base = smem + stage * SM::STAGE_ELEMS;
+#pragma unroll
+    for (int r = 0; r < G_PER_T; ++r) {
+      const int g = tid + r * kBwdThreads;
+      if (g < GROUPS) {
+        const int dc = g % C8, kg = g / C8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          *reinterpret_cast<u32x4*>(base + SM::K_OFF + (kg * 4 + i) * SM::RS + dc * 8) = kreg[r][i];
+          *reinterpret_cast<u32x4*>(base + SM::V_OFF + (kg * 4 + i) * SM::RS + dc * 8) = vreg[r][i];
+        }
+        store_transposed_4x8(base + SM::KT_OFF, kg, dc, kreg[r]);
+      }
+    }
+  };
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    const bool has_next = t + 1 < n_tiles;
+    if (has_next) load_tile(t + 1);
+    const int k0 = t * BN;
+    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    if (!skip) {
+      const __bf16* base = smem + stage * SM::STAGE_ELEMS;
+      const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw0)) || (k0 + BN > N);
+      bf16x8 dsb[4];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        f32x16 sacc = f32x16{}, dpacc = f32x16{};
+        const __bf16* krow = base + SM::K_OFF + (kbk * 32 + l32) * SM::RS + 8 * hh;
+        const __bf16* vrow = base + SM::V_OFF + (kbk * 32 + l32) * SM::RS + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc);
+          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * s), dof[s], dpacc);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = fast_exp2(sacc[e] * scale_log2 - my_lse2);
+          if (need_mask) {
+            const int key = k0 + kbk * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool masked = (key >= N) || (CAUSAL && key > my_q);
+            p = masked ? 0.f : p;
+          }
+          dsb[kbk * 2 + (e >> 3)][e & 7] = (__bf16)(p * (dpacc[e] - my_dlt));
+        }
+      }
+#pragma unroll
+      for (int dbk = 0; dbk < DB; ++dbk) {
+        const int d = dbk * 32 + l32;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          dqacc[dbk] = mfma32(load_tr_operand(base + SM::KT_OFF, d, st, hh), dsb[st], dqacc[dbk]);
+        }
+      }
+    }
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active || my_q >= N) return;
+  __bf16* orow = dq + ((int64_t)b * N + my_q) * q_rs + (int64_t)hq * D;
+#pragma unroll
+  for (int dbk = 0; dbk < DB; ++dbk) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w[0] = pack_bf16x2(dqacc[dbk][4 * j + 0] * scale, dqacc[dbk][4 * j + 1] * scale);
+      w[1] = pack_bf16x2(dqacc[dbk][4 * j + 2] * scale, dqacc[dbk][4 * j + 3] * scale);
+      *reinterpret_cast<u32x2*>(orow + dbk * 32 + 8 * j + 4 * hh) = w;
+    }
+  }
+}
+
+template <typename K>
+hipError_t set_smem(K kern, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)bytes);
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const BwdArgs& a, float* delta) {
+  const float scale_log2 = a.scale * kLog2e;
+  {
+    const int64_t threads = (int64_t)a.B * a.N * a.Hq * (D / 8);
+    const int64_t grid = (threads + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)grid), dim3(256), 0, a.stream,
+                       (const __bf16*)a.o, (const __bf16*)a.dout, delta, a.B, a.Hq, a.N);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nkt = (a.N + 127) / 128;
+    const int64_t grid = (int64_t)nkt * a.B * a.Hkv;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    auto kern = bwd_dkdv_kernel<D, CAUSAL>;
+    hipError_t e = set_smem(kern, DkdvSmem<D>::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DkdvSmem<D>::BYTES, a.stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
+                       scale_log2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    const int nqt = (a.N + 127) / 128;
+    const int64_t grid = (int64_t)nqt * a.B * a.Hq;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    auto kern = bwd_dq_kernel<D, CAUSAL>;
+    hipError_t e = set_smem(kern, DqSmem<D>::BYTES);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                       (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdArgs& a, float* delta) {
+  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a, delta) : launch_bwd_t<64, false>(a, delta);
+  return a.causal ? launch_bwd_t<128, true>(a, delta) : launch_bwd_t<128, false>(a, delta);
+}
+
+}  // namespace fa

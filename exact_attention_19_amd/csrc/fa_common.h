@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// 32x32x16 bf16 MFMA (gfx950): D[32x32] += A[32x16] * B[16x32].
+// Lane l supplies A row (l % 32), k = 8*(l/32) .. +7 and B column (l % 32),
+// k = 8*(l/32) .. +7; it receives D column (l % 32), rows
+// 8*j + 4*(l/32) + i in element 4*j + i.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16x2 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Low 16 bits of a and of b into one dword: (a.lo, b.lo).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+// High 16 bits of a and of b into one dword: (a.hi, b.hi).
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+template <typename T>
+__device__ __forceinline__ T max3(T a, T b, T c) { return fmaxf(fmaxf(a, b), c); }
+
+// Value of lane (l ^ 32): exchange between the two halves of the wave.
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over LPT consecutive lanes (LPT = 8 or 16); every lane of the group
+// receives the same total (each pairing adds two equal-order partial sums).
+template <int LPT>
+__device__ __forceinline__ float row_group_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += dpp_f<0x141>(x);  // row_half_mirror: pairs the two quads of each 8 lanes
+  if (LPT == 16) x += dpp_f<0x140>(x);  // row_mirror: pairs the two halves of 16 lanes
+  return x;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+// 8-element bf16 dot product accumulated in fp32 (v_dot2_f32_bf16). Each
+// vector element is copied into a scalar before the bit cast: casting the
+// indexed element in place made hipcc (ROCm 7.2) load element 0 only.
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = a[w], y = b[w];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(x), as_bf16x2(y), acc, false);
+  }
+  return acc;
+}
+
+// Transposed 64-wide tiles in LDS (V^T in the forward, Q^T / dO^T / K^T in
+// the backward): D rows of 64 bf16 (128 bytes) each, holding one head-dim
+// index per row and 64 sequence positions along the row.
+//
+// Position of sequence group kg (4 consecutive positions, kg = 0..15) inside
+// the row. Within each group of 16 positions, groups of 4 are stored in the
+// order 0, 2, 1, 3: the order in which a 32x32 MFMA accumulator hands them to
+// one 16-deep MFMA step (lanes 0-31 hold positions 0-3 and 8-11, lanes 32-63
+// hold 4-7 and 12-15). A lane reading the 16 bytes at logical offset
+// 16*step + 8*(l/32) then gets exactly the 8 positions its accumulator half
+// holds, so the permutation cancels in the product.
+__device__ __forceinline__ int tr_pos_of_group4(int kg) {
+  const int in16 = kg & 3;
+  const int perm = (in16 == 1) ? 2 : (in16 == 2 ? 1 : in16);
+  return (kg >> 2) * 16 + perm * 4;
+}
+
+// XOR swizzle of the eight 16-byte units of a transposed row, so that both
+// the transposing writes (rows 8 apart) and the MFMA operand reads
+// (consecutive rows) spread over the LDS banks.
+__device__ __forceinline__ int tr_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
+// Write the 4 (positions) x 8 (head dims) block held in `rows` (four 16-byte
+// rows, one per position) transposed into a 64-wide tile `tr`: 8 rows
+// (dims 8*dc .. 8*dc+7) of 4 positions each.
+__device__ __forceinline__ void store_transposed_4x8(__bf16* tr, int kg, int dc, const u32x4 (&rows)[4]) {
+  const int pos = tr_pos_of_group4(kg);
+  const int unit = pos >> 3, half = (pos >> 2) & 1;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int d = dc * 8 + j;
+    const int w = j >> 1;
+    const uint32_t a0 = rows[0][w], a1 = rows[1][w], a2 = rows[2][w], a3 = rows[3][w];
+    u32x2 out;
+    if (j & 1) {
+      out[0] = (a0 >> 16) | (a1 & 0xffff0000u);
+      out[1] = (a2 >> 16) | (a3 & 0xffff0000u);
+    } else {
+      out[0] = (a0 & 0xffffu) | (a1 << 16);
+      out[1] = (a2 & 0xffffu) | (a3 << 16);
+    }
+    const int u = unit ^ tr_swz(d);
+    *reinterpret_cast<u32x2*>(tr + d * 64 + u * 8 + half * 4) = out;
+  }
+}
+
+// MFMA A operand from a transposed tile: row d, logical 16-byte unit
+// 2*step + half.
+__device__ __forceinline__ bf16x8 load_tr_operand(const __bf16* tr, int d, int step, int half) {
+  const int u = (2 * step + half) ^ tr_swz(d);
+  return *reinterpret_cast<const bf16x8*>(tr + d * 64 + u * 8);
+}
+
+}  // namespace fa

@@ -1,0 +1,367 @@
+// Forward attention kernels for gfx950 (MI355X).
+//
+// O = softmax(Q K^T * scale [+ causal mask]) V, computed tile by tile
+// (Qiita FlashAttention tutorial, sections 4.2-4.3; abeam.tech summary of the
+// FlashAttention paper, "Tiling によるメモリアクセス削減" and "Softmax を
+// ブロック単位で正しく計算する"): a workgroup keeps a block of query rows in
+// registers, streams key/value tiles through LDS, keeps a running row
+// maximum and exp-sum, rescales the output accumulator when the maximum
+// grows, and writes only O and the row logsumexp.
+//
+// bf16 path, per wave (32 query rows):
+//   S^T = K * Q^T with the 32x32x16 bf16 MFMA, so that every lane holds the
+//   scores of a single query row (lane l: query l % 32, half the keys). Row
+//   maximum and sum are then in-lane, plus one exchange with lane l ^ 32.
+//   O^T += V^T * P^T with the same MFMA: the score accumulator, rounded to
+//   bf16, is already the B operand once the keys of each 16-key step are
+//   taken in the order the accumulator holds them; V^T is kept in LDS with
+//   its keys stored in that same order, so the permutation cancels.
+// fp32 path: a plain VALU kernel (one query row per lane), used for fp32
+// inputs, where P must not be rounded.
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kBN = 64;  // keys per tile
+
+template <int D, int NWAVES>
+struct FwdSmem {
+  static constexpr int KS = D + 8;                      // K row stride (elements), 16-byte pad
+  static constexpr int K_ELEMS = kBN * KS;
+  static constexpr int VT_ELEMS = D * kBN;              // V^T: D rows of kBN keys, no pad
+  static constexpr int STAGE_ELEMS = K_ELEMS + VT_ELEMS;
+  static constexpr int BYTES = 2 * STAGE_ELEMS * 2;     // two stages, bf16
+};
+
+template <int D, int NWAVES, bool CAUSAL>
+__global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N,
+    float scale_log2, int num_q_tiles) {
+  constexpr int BM = NWAVES * 32;
+  constexpr int NT = NWAVES * 64;
+  constexpr int DS = D / 16;      // MFMA k-steps over the head dim
+  constexpr int DB = D / 32;      // 32-row blocks of O^T
+  constexpr int C8 = D / 8;       // 16-byte chunks per row
+  using SM = FwdSmem<D, NWAVES>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  // Heaviest causal tiles first; consecutive workgroups take different heads.
+  const int BH = B * Hq;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int rank = bid / BH;
+  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+
+  const int64_t q_row_stride = (int64_t)Hq * D;
+  const int64_t kv_row_stride = (int64_t)Hkv * D;
+  const __bf16* qb = q + ((int64_t)b * N) * q_row_stride + (int64_t)hq * D;
+  const __bf16* kb = k + ((int64_t)b * N) * kv_row_stride + (int64_t)hk * D;
+  const __bf16* vb = v + ((int64_t)b * N) * kv_row_stride + (int64_t)hk * D;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;          // first query row of this wave
+  const int my_q = qw0 + l32;              // query row of this lane
+  const bool wave_active = qw0 < N;
+
+  // Q fragments: B operand of S^T = K Q^T. Lane holds Q[my_q][16 s + 8 hh .. +7].
+  bf16x8 qf[DS];
+  {
+    const bool ok = my_q < N;
+    const __bf16* qrow = qb + (int64_t)(ok ? my_q : 0) * q_row_stride + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  int kv_end = N;
+  if (CAUSAL) kv_end = min(N, q0 + BM);
+  const int n_tiles = (kv_end + kBN - 1) / kBN;
+
+  // Global -> register staging of one K/V tile.
+  constexpr int K_CHUNKS = kBN * C8;                 // 16-byte chunks of the K tile
+  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
+  constexpr int V_GROUPS = (kBN / 4) * C8;           // (4 keys x 8 dims) groups of V
+  constexpr int V_PER_T = (V_GROUPS + NT - 1) / NT;
+  u32x4 kreg[K_PER_T];
+  u32x4 vreg[V_PER_T][4];
+
+  auto load_tile = [&](int t) {
+    const int k0 = t * kBN;
+#pragma unroll
+    for (int r = 0; r < K_PER_T; ++r) {
+      const int c = tid + r * NT;
+      const int row = c / C8, col = c % C8;
+      const int key = k0 + row;
+      kreg[r] = (c < K_CHUNKS && key < N)
+                    ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kv_row_stride + col * 8)
+                    : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < V_PER_T; ++r) {
+      const int g = tid + r * NT;
+      const int dc = g % C8, kg = g / C8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + kg * 4 + i;
+        vreg[r][i] = (g < V_GROUPS && key < N)
+                         ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kv_row_stride + dc * 8)
+                         : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  auto store_tile = [&](int stage) {
+    __bf16* ks = smem + stage * SM::STAGE_ELEMS;
+    __bf16* vt = ks + SM::K_ELEMS;
+#pragma unroll
+    for (int r = 0; r < K_PER_T; ++r) {
+      const int c = tid + r * NT;
+      if (c < K_CHUNKS) {
+        const int row = c / C8, col = c % C8;
+        *reinterpret_cast<u32x4*>(ks + row * SM::KS + col * 8) = kreg[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < V_PER_T; ++r) {
+      const int g = tid + r * NT;
+      if (g < V_GROUPS) {
+        store_transposed_4x8(vt, g / C8, g % C8, vreg[r]);
+      }
+    }
+  };
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = kNegInf;  // running max of the scaled scores (log2 units)
+  float l_run = 0.f;      // this lane's share of the running exp-sum
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int stage = t & 1;
+    const bool has_next = (t + 1) < n_tiles;
+    if (has_next) load_tile(t + 1);
+
+    const int k0 = t * kBN;
+    const bool wave_skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    if (!wave_skip) {
+      const __bf16* ks = smem + stage * SM::STAGE_ELEMS;
+      const __bf16* vt = ks + SM::K_ELEMS;
+      // S^T for the two 32-key blocks of the tile.
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+        sacc[kbk] = f32x16{};
+        const __bf16* krow = ks + (kbk * 32 + l32) * SM::KS + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * s);
+          sacc[kbk] = mfma32(a, qf[s], sacc[kbk]);
+        }
+      }
+      // Scale to log2 units and mask.
+      const bool need_mask = (CAUSAL && (k0 + kBN - 1 > qw0)) || (k0 + kBN > N);
+      float mt = kNegInf;
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float x = sacc[kbk][e] * scale_log2;
+          if (need_mask) {
+            const int key = k0 + kbk * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+            const bool masked = (key >= N) || (CAUSAL && key > my_q);
+            x = masked ? kNegInf : x;
+          }
+          sacc[kbk][e] = x;
+          mt = fmaxf(mt, x);
+        }
+      }
+      mt = fmaxf(mt, swap_halves(mt));
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int kbk = 0; kbk < 2; ++kbk) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float p = fast_exp2(sacc[kbk][e] - m_use);
+          psum += p;
+          pb[kbk * 2 + (e >> 3)][e & 7] = (__bf16)p;
+        }
+      }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      }
+      // O^T += V^T P^T.
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 32 + l32;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          bf16x8 a = load_tr_operand(vt, d, st, hh);
+          oacc[db] = mfma32(a, pb[st], oacc[db]);
+        }
+      }
+    }
+
+    if (has_next) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + swap_halves(l_run);
+  if (my_q < N) {
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    __bf16* orow = o + ((int64_t)b * N + my_q) * q_row_stride + (int64_t)hq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hh) = w;
+      }
+    }
+    if (hh == 0) {
+      lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + __log2f(l_tot)) * kLn2;
+    }
+  }
+}
+
+// fp32 path: one query row per lane, 32-key tiles staged in LDS.
+template <int D>
+__global__ __launch_bounds__(64, 1) void fwd_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    float* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
+    int causal, int num_q_tiles) {
+  constexpr int TK = 32;
+  __shared__ float ks[TK][D];
+  __shared__ float vs[TK][D];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x % (B * Hq);
+  const int qt = blockIdx.x / (B * Hq);
+  const int b = bh / Hq, hq = bh % Hq, hk = hq / (Hq / Hkv);
+  const int my_q = qt * 64 + tid;
+  const int64_t qs = (int64_t)Hq * D, kvs = (int64_t)Hkv * D;
+  const float* qrow = q + ((int64_t)b * N + min(my_q, N - 1)) * qs + (int64_t)hq * D;
+  float qr[D], acc[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) { qr[c] = qrow[c]; acc[c] = 0.f; }
+  float m_run = kNegInf, l_run = 0.f;
+  int kv_end = N;
+  if (causal) kv_end = min(N, qt * 64 + 64);
+  for (int k0 = 0; k0 < kv_end; k0 += TK) {
+    __syncthreads();
+    for (int i = tid; i < TK * D; i += 64) {
+      const int r = i / D, c = i % D;
+      const int key = k0 + r;
+      const int64_t off = ((int64_t)b * N + key) * kvs + (int64_t)hk * D + c;
+      ks[r][c] = key < N ? k[off] : 0.f;
+      vs[r][c] = key < N ? v[off] : 0.f;
+    }
+    __syncthreads();
+    float s[TK];
+    float mt = kNegInf;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) dot = fmaf(qr[c], ks[j][c], dot);
+      const int key = k0 + j;
+      const bool masked = key >= N || (causal && key > my_q);
+      s[j] = masked ? kNegInf : dot * scale_log2;
+      mt = fmaxf(mt, s[j]);
+    }
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int c = 0; c < D; ++c) acc[c] *= alpha;
+#pragma unroll
+    for (int j = 0; j < TK; ++j) {
+      const float p = exp2f(s[j] - m_use);
+      l_run += p;
+#pragma unroll
+      for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vs[j][c], acc[c]);
+    }
+  }
+  if (my_q < N) {
+    const bool empty = !(l_run > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_run;
+    float* orow = o + ((int64_t)b * N + my_q) * qs + (int64_t)hq * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
+    lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + log2f(l_run)) * kLn2;
+  }
+}
+
+template <int D, int NWAVES, bool CAUSAL>
+hipError_t launch_bf16(const FwdArgs& a) {
+  constexpr int BM = NWAVES * 32;
+  const int num_q_tiles = (a.N + BM - 1) / BM;
+  const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const size_t smem = FwdSmem<D, NWAVES>::BYTES;
+  auto kern = fwd_bf16_kernel<D, NWAVES, CAUSAL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_f32(const FwdArgs& a) {
+  const int num_q_tiles = (a.N + 63) / 64;
+  const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(64), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
+                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, a.causal, num_q_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdArgs& a) {
+  if (a.dtype == kDtypeF32) {
+    return a.d == 64 ? launch_f32<64>(a) : launch_f32<128>(a);
+  }
+  if (a.d == 64) {
+    return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
+  }
+  return a.causal ? launch_bf16<128, 4, true>(a) : launch_bf16<128, 4, false>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,68 @@
+// Host-side interfaces between the C ABI (fa_api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kDtypeBf16 = 0;
+constexpr int kDtypeF32 = 1;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  int causal;
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* seqlens;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d;
+  float scale;
+  hipStream_t stream;
+};
+
+// Decode splits the cache into chunks of this many rows unless told otherwise.
+constexpr int kDecodeDefaultChunk = 512;
+// Query heads that one decode workgroup serves from a single read of K/V.
+constexpr int kDecodeMaxHeadsPerGroup = 4;
+
+hipError_t launch_fwd(const FwdArgs& a);
+
+// Backward: D = rowsum(dO * O) is written to `delta` ([B, Hq, N] float32).
+hipError_t launch_bwd(const BwdArgs& a, float* delta);
+
+int decode_heads_per_group(int Hq, int Hkv);
+void decode_split_plan(int N, int num_splits, int* chunk, int* nsplit);
+hipError_t launch_decode(const DecodeArgs& a, float* part_o, float* part_lse, int chunk, int nsplit);
+
+}  // namespace fa

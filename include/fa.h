@@ -1,0 +1,132 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library (libfa_mi355x.so).
+ *
+ * Every entry point computes exact scaled-dot-product attention
+ *     O = softmax(Q K^T * scale [+ causal mask]) V
+ * as defined in the Qiita FlashAttention tutorial (GeneLab_999), section 2.2,
+ * and in the hysenlabs digest of the flash-attention README (section on
+ * outputs: softmax(Q @ K^T * softmax_scale) @ V, with MQA/GQA when the number
+ * of query heads is a multiple of the number of key/value heads). The scores
+ * S and probabilities P are never written to device memory: Q, K and V tiles
+ * are staged on chip and an online softmax (tutorial section 4.3) carries the
+ * per-row running maximum and sum (abeam.tech summary of the FlashAttention
+ * paper, "Softmax をブロック単位で正しく計算する").
+ *
+ * Conventions shared by all entry points
+ * --------------------------------------
+ * Layouts (row-major, last dimension contiguous, no padding between rows):
+ *   q, o, dout, dq : [B, N, Hq,  d]
+ *   k, v, dk, dv   : [B, N, Hkv, d]
+ *   lse            : [B, Hq, N] float32, natural-log logsumexp of the scaled,
+ *                    masked scores of each query row: log sum_j exp(S_ij).
+ * GQA grouping: query head h reads key/value head h / (Hq / Hkv).
+ * Causal masking keeps key j for query i iff j <= i (queries and keys have
+ *   the same length N here, where bottom-right and top-left alignment agree).
+ * dtype: FA_BF16 (bfloat16 storage, float32 accumulation; outputs rounded to
+ *   nearest even) or FA_FP32 (float32 throughout; fa_fwd only).
+ * Supported head dims: d = 64 or 128.
+ *
+ * Ownership: every pointer is device memory owned by the caller (including
+ *   workspaces). The library allocates and frees nothing, never synchronises
+ *   the device, and keeps no state except a thread-local error message.
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) and the call returns after enqueueing. Results are valid
+ *   once the stream has reached that point.
+ * Errors: arguments are validated before any HIP call; on failure nothing is
+ *   launched and a non-zero fa_status is returned. fa_last_error() then
+ *   returns a message for the calling thread. No C++ exception crosses the
+ *   ABI. NaN or Inf in the inputs propagate to the outputs; they are not
+ *   detected.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, non-positive size, Hq % Hkv != 0,
+                             non-finite or non-positive scale, bad cache length range */
+  FA_ERR_UNSUPPORTED = 2, /* head dim or dtype not implemented for this entry point */
+  FA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace_bytes query */
+  FA_ERR_HIP = 4          /* a HIP launch failed; fa_last_error() has hipGetErrorString */
+} fa_status;
+
+typedef enum { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+/*
+ * Forward pass: O and the per-row logsumexp.
+ * Defined by the attention formula above; the forward keeps only the
+ * normalisation statistic (LSE) needed to recompute attention in the backward
+ * pass (abeam summary, "用語解説: Recomputation").
+ *   q [B,N,Hq,d], k/v [B,N,Hkv,d] in: dtype;  o [B,N,Hq,d] out: dtype;
+ *   lse [B,Hq,N] float32 out (may not be NULL).
+ * Pointers must be 16-byte aligned (lse: 4-byte).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                 int dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd needs for these sizes (256-byte aligned). */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+
+/*
+ * Backward pass: gradients of L = sum(O * dout) with respect to Q, K and V,
+ * recomputing the attention tiles from Q, K and the saved LSE instead of
+ * storing S or P (abeam summary, "学習時の backward では再計算を使う").
+ *   q, k, v: as in fa_fwd; o [B,N,Hq,d] and lse: the outputs of fa_fwd for
+ *   the same inputs; dout [B,N,Hq,d]: upstream gradient.
+ *   dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] out (dk/dv sum over the query heads of
+ *   each group). bf16 only. The result is deterministic (no atomics).
+ *   workspace: device memory of at least fa_bwd_workspace_bytes(...) bytes,
+ *   256-byte aligned; its contents on entry do not matter.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes,
+                 int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                 int dtype, void* stream);
+
+/* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it). */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
+
+/*
+ * Decode against a KV cache: one new query token per sequence attends the
+ * first cache_seqlens[b] rows of that sequence's cache (the inference path
+ * of flash_attn_with_kvcache in the hysenlabs digest, "出力と運用記録"; the
+ * v2.2 changelog entry adds it for short queries). The cache is read in
+ * splits along the sequence, each split producing a partial (O, LSE), and a
+ * second kernel merges the partials with LSE weights.
+ *   q [B,Hq,d] in; k_cache/v_cache [B,N,Hkv,d] in (N = cache capacity;
+ *   rows >= cache_seqlens[b] are never read); cache_seqlens: int32 [B] in
+ *   device memory, each in [1, N] (a value outside that range makes that
+ *   sequence's output O = 0, LSE = -inf rather than reading out of range);
+ *   o [B,Hq,d] out; lse [B,Hq] float32 out, or NULL.
+ *   causal: accepted for symmetry; with one query aligned to the bottom-right
+ *   corner every cached key is visible, so it does not change the result.
+ *   num_splits: number of sequence splits (0 = chosen by the library from N).
+ *   workspace: at least fa_decode_workspace_bytes(..., num_splits) bytes.
+ * bf16 only.
+ */
+fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cache_seqlens, void* o, float* lse,
+                            void* workspace, size_t workspace_bytes,
+                            int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                            int num_splits, int dtype, void* stream);
+
+/* Message for the last non-FA_OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version string. */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

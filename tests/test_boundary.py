@@ -1,0 +1,131 @@
+"""C ABI boundary checks that need no GPU: the library loads, exports every
+function include/fa.h declares with the argument count the binding uses, and
+rejects invalid arguments with the documented status before any HIP call."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from exact_attention_19_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+FAKE = 0x10000  # an aligned, never-dereferenced address: every case below fails validation first
+MISALIGNED = 0x10002
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"\b(?:fa_status|size_t|const char\*)\s+(fa_\w+)\s*\(([^)]*)\)\s*;", text):
+        args = [a for a in m.group(2).split(",") if a.strip() and a.strip() != "void"]
+        decls[m.group(1)] = len(args)
+    return decls
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_entry_points():
+    decls = _declared()
+    for name in ("fa_fwd", "fa_bwd", "fa_decode_kvcache", "fa_bwd_workspace_bytes",
+                 "fa_decode_workspace_bytes", "fa_last_error", "fa_version"):
+        assert name in decls, name
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name, nargs in _declared().items():
+        assert hasattr(lib, name), f"{name} not exported"
+        assert name in _lib.SIGNATURES, f"{name} not bound"
+        assert len(_lib.SIGNATURES[name][1]) == nargs, f"{name}: binding has wrong argument count"
+
+
+def _fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1, causal=0,
+         dtype=_lib.FA_BF16):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(q=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(lse=None), _lib.FA_ERR_INVALID_ARG),
+    (dict(o=MISALIGNED), _lib.FA_ERR_INVALID_ARG),
+    (dict(B=0), _lib.FA_ERR_INVALID_ARG),
+    (dict(N=-3), _lib.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), _lib.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), _lib.FA_ERR_INVALID_ARG),
+    (dict(d=96), _lib.FA_ERR_UNSUPPORTED),
+    (dict(d=256), _lib.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_validation(lib, kw, status):
+    assert _fwd(lib, **kw) == status
+    assert lib.fa_last_error().decode().startswith("fa_fwd")
+
+
+def test_bwd_validation(lib):
+    args = [FAKE] * 10 + [1 << 20, 1, 4, 2, 64, 128, 0.1, 1, _lib.FA_BF16, None]
+    bad_dtype = list(args)
+    bad_dtype[18] = _lib.FA_FP32
+    assert lib.fa_bwd(*bad_dtype) == _lib.FA_ERR_UNSUPPORTED
+    no_ws = list(args)
+    no_ws[9] = None
+    assert lib.fa_bwd(*no_ws) == _lib.FA_ERR_WORKSPACE
+    small = list(args)
+    small[10] = lib.fa_bwd_workspace_bytes(1, 4, 2, 64, 128) - 1
+    assert lib.fa_bwd(*small) == _lib.FA_ERR_WORKSPACE
+    bad_heads = list(args)
+    bad_heads[12], bad_heads[13] = 3, 2
+    assert lib.fa_bwd(*bad_heads) == _lib.FA_ERR_INVALID_ARG
+    assert "fa_bwd" in lib.fa_last_error().decode()
+
+
+def test_decode_validation(lib):
+    ws = lib.fa_decode_workspace_bytes(2, 8, 2, 1000, 128, 0)
+    args = [FAKE] * 7 + [ws, 2, 8, 2, 1000, 128, 0.1, 0, 0, _lib.FA_BF16, None]
+    neg = list(args)
+    neg[15] = -1  # num_splits
+    assert lib.fa_decode_kvcache(*neg) == _lib.FA_ERR_INVALID_ARG
+    small = list(args)
+    small[7] = ws - 4
+    assert lib.fa_decode_kvcache(*small) == _lib.FA_ERR_WORKSPACE
+    nolse_bad = list(args)
+    nolse_bad[3] = None  # cache_seqlens
+    assert lib.fa_decode_kvcache(*nolse_bad) == _lib.FA_ERR_INVALID_ARG
+    fp32 = list(args)
+    fp32[16] = _lib.FA_FP32  # dtype
+    assert lib.fa_decode_kvcache(*fp32) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    assert lib.fa_bwd_workspace_bytes(1, 96, 96, 8192, 128) == 96 * 8192 * 4
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1, 1, 64) == 0
+    # default split: 512-row chunks -> 64 splits for a 32768-row cache
+    o_bytes = 64 * 32 * 64 * 128 * 4
+    lse_bytes = 64 * 32 * 64 * 4
+    assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 128, 0) == o_bytes + lse_bytes
+    # one split
+    assert lib.fa_decode_workspace_bytes(2, 4, 2, 100, 64, 1) == (2 * 4 * 64 * 4 + 255) // 256 * 256 + 256
+
+
+def test_binding_rejects_host_tensors():
+    import exact_attention_19_amd as fa
+
+    x = torch.zeros(1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x)
+
+
+def test_error_message_is_per_call(lib):
+    assert _fwd(lib, d=80) == _lib.FA_ERR_UNSUPPORTED
+    assert "d=80" in lib.fa_last_error().decode()
+    assert _fwd(lib, B=0) == _lib.FA_ERR_INVALID_ARG
+    assert "sizes" in lib.fa_last_error().decode()
+    assert isinstance(lib.fa_version(), bytes) and ctypes.sizeof(ctypes.c_size_t) == 8
