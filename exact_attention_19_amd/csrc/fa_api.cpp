@@ -74,6 +74,40 @@ void decode_ws_layout(int B, int Hq, int N, int d, int num_splits, int* chunk, i
   *lse_bytes = round_up((size_t)B * Hq * (size_t)(*nsplit) * sizeof(float), 256);
 }
 
+fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                     int dtype, void* stream) {
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  const bool all = stage < 0;
+  if (all || stage == 0) {
+    FA_TRY(check_ptr(fn, "o", o, 16));
+    FA_TRY(check_ptr(fn, "dout", dout, 16));
+  }
+  if (all || stage >= 1) {
+    FA_TRY(check_ptr(fn, "q", q, 16));
+    FA_TRY(check_ptr(fn, "k", k, 16));
+    FA_TRY(check_ptr(fn, "v", v, 16));
+    FA_TRY(check_ptr(fn, "dout", dout, 16));
+    FA_TRY(check_ptr(fn, "lse", lse, 4));
+  }
+  if (all || stage == 1) {
+    FA_TRY(check_ptr(fn, "dk", dk, 16));
+    FA_TRY(check_ptr(fn, "dv", dv, 16));
+  }
+  if (all || stage == 2) FA_TRY(check_ptr(fn, "dq", dq, 16));
+  const size_t need = bwd_ws_bytes(B, Hq, N);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
+                reinterpret_cast<hipStream_t>(stream)};
+  float* delta = static_cast<float*>(workspace);
+  return hip_status(fn, all ? fa::launch_bwd(a, delta) : fa::launch_bwd_stage(a, delta, stage));
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,26 +141,16 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                  int N, int d, float scale, int causal, int dtype, void* stream) {
-  static const char* fn = "fa_bwd";
-  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
-  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
-  FA_TRY(check_ptr(fn, "q", q, 16));
-  FA_TRY(check_ptr(fn, "k", k, 16));
-  FA_TRY(check_ptr(fn, "v", v, 16));
-  FA_TRY(check_ptr(fn, "o", o, 16));
-  FA_TRY(check_ptr(fn, "dout", dout, 16));
-  FA_TRY(check_ptr(fn, "lse", lse, 4));
-  FA_TRY(check_ptr(fn, "dq", dq, 16));
-  FA_TRY(check_ptr(fn, "dk", dk, 16));
-  FA_TRY(check_ptr(fn, "dv", dv, 16));
-  const size_t need = bwd_ws_bytes(B, Hq, N);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
-                reinterpret_cast<hipStream_t>(stream)};
-  return hip_status(fn, fa::launch_bwd(a, static_cast<float*>(workspace)));
+  return bwd_common("fa_bwd", -1, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, N, d,
+                    scale, causal, dtype, stream);
+}
+
+fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (stage < 0 || stage > 2) return fail(FA_ERR_INVALID_ARG, "fa_bwd_stage: stage %d is not 0, 1 or 2", stage);
+  return bwd_common("fa_bwd_stage", stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq,
+                    Hkv, N, d, scale, causal, dtype, stream);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits) {

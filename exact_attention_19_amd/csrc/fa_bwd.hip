@@ -439,18 +439,17 @@ hipError_t set_smem(K kern, size_t bytes) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, float* delta) {
+hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const float scale_log2 = a.scale * kLog2e;
-  {
+  if (stage == 0) {
     const int64_t threads = (int64_t)a.B * a.N * a.Hq * (D / 8);
     const int64_t grid = (threads + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)grid), dim3(256), 0, a.stream,
                        (const __bf16*)a.o, (const __bf16*)a.dout, delta, a.B, a.Hq, a.N);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  {
+  if (stage == 1) {
     const int nkt = (a.N + 127) / 128;
     const int64_t grid = (int64_t)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -461,30 +460,33 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta) {
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                        (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
                        scale_log2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
-  {
-    const int nqt = (a.N + 127) / 128;
-    const int64_t grid = (int64_t)nqt * a.B * a.Hq;
-    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-    auto kern = bwd_dq_kernel<D, CAUSAL>;
-    hipError_t e = set_smem(kern, DqSmem<D>::BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const int nqt = (a.N + 127) / 128;
+  const int64_t grid = (int64_t)nqt * a.B * a.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  auto kern = bwd_dq_kernel<D, CAUSAL>;
+  hipError_t e = set_smem(kern, DqSmem<D>::BYTES);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
+                     (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage) {
+  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a, delta, stage) : launch_bwd_t<64, false>(a, delta, stage);
+  return a.causal ? launch_bwd_t<128, true>(a, delta, stage) : launch_bwd_t<128, false>(a, delta, stage);
+}
+
 hipError_t launch_bwd(const BwdArgs& a, float* delta) {
-  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a, delta) : launch_bwd_t<64, false>(a, delta);
-  return a.causal ? launch_bwd_t<128, true>(a, delta) : launch_bwd_t<128, false>(a, delta);
+  for (int stage = 0; stage < 3; ++stage) {
+    hipError_t e = launch_bwd_stage(a, delta, stage);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -59,6 +59,8 @@ constexpr int kDecodeMaxHeadsPerGroup = 4;
 hipError_t launch_fwd(const FwdArgs& a);
 
 // Backward: D = rowsum(dO * O) is written to `delta` ([B, Hq, N] float32).
+// Stage 0 computes D, stage 1 dK and dV, stage 2 dQ; launch_bwd runs all three.
+hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage);
 hipError_t launch_bwd(const BwdArgs& a, float* delta);
 
 int decode_heads_per_group(int Hq, int Hkv);

@@ -92,6 +92,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                  int dtype, void* stream);
 
+/*
+ * One stage of fa_bwd, for callers that schedule or time the stages
+ * separately. fa_bwd is exactly stage 0, then 1, then 2 on one stream, with
+ * the same arguments and workspace (stage 0 writes D = rowsum(dO * O) into
+ * the workspace, stages 1 and 2 read it):
+ *   stage 0: D;  stage 1: dK and dV;  stage 2: dQ.
+ * Pointers a stage does not use may be NULL (stage 0 reads only o, dout;
+ * stage 1 writes only dk, dv; stage 2 writes only dq). Any other stage
+ * number returns FA_ERR_INVALID_ARG.
+ */
+fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                       int dtype, void* stream);
+
 /* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
 
