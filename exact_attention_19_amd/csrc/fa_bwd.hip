@@ -106,14 +106,15 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
   const int my_key = kw0 + l32;
   const bool wave_active = kw0 < N;
 
+  // Rows past N read row N-1 (their dK/dV are never written), so no load is
+  // predicated.
   bf16x8 kf[DS], vf[DS];
   {
-    const bool ok = my_key < N;
-    const int64_t off = ((int64_t)b * N + (ok ? my_key : 0)) * kv_rs + (int64_t)hk * D + 8 * hh;
+    const int64_t off = ((int64_t)b * N + min(my_key, N - 1)) * kv_rs + (int64_t)hk * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(k + off + 16 * s) : u32x4{0, 0, 0, 0});
-      vf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(v + off + 16 * s) : u32x4{0, 0, 0, 0});
+      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k + off + 16 * s));
+      vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(v + off + 16 * s));
     }
   }
 
@@ -130,17 +131,20 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
     const int q0 = (qt0 + it % per_head) * BQ;
     const __bf16* qb = q + (int64_t)b * N * q_rs + (int64_t)hq * D;
     const __bf16* db = dout + (int64_t)b * N * q_rs + (int64_t)hq * D;
+    // Query rows past N are read as row N-1; their LSE is set to +inf below,
+    // which makes their probabilities (and so their dS) exactly 0.
 #pragma unroll
     for (int r = 0; r < G_PER_T; ++r) {
       const int g = tid + r * kBwdThreads;
       const int dc = g % C8, rg = g / C8;
+      if (GROUPS % kBwdThreads == 0 || g < GROUPS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = q0 + rg * 4 + i;
-        const bool ok = g < GROUPS && row < N;
-        const int64_t off = (int64_t)row * q_rs + dc * 8;
-        qreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(qb + off) : u32x4{0, 0, 0, 0};
-        dreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(db + off) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+          const int row = min(q0 + rg * 4 + i, N - 1);
+          const int64_t off = (int64_t)row * q_rs + dc * 8;
+          qreg[r][i] = *reinterpret_cast<const u32x4*>(qb + off);
+          dreg[r][i] = *reinterpret_cast<const u32x4*>(db + off);
+        }
       }
     }
     if (tid < BQ) {
@@ -310,20 +314,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   const int my_q = qw0 + l32;
   const bool wave_active = qw0 < N;
 
+  // Rows past N read row N-1 (their dQ is never written).
   bf16x8 qf[DS], dof[DS];
-  float my_lse2 = __builtin_inff(), my_dlt = 0.f;
+  float my_lse2, my_dlt;
   {
-    const bool ok = my_q < N;
-    const int64_t off = ((int64_t)b * N + (ok ? my_q : 0)) * q_rs + (int64_t)hq * D + 8 * hh;
+    const int row = min(my_q, N - 1);
+    const int64_t off = ((int64_t)b * N + row) * q_rs + (int64_t)hq * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      qf[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(q + off + 16 * s) : u32x4{0, 0, 0, 0});
-      dof[s] = __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(dout + off + 16 * s) : u32x4{0, 0, 0, 0});
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off + 16 * s));
+      dof[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dout + off + 16 * s));
     }
-    if (ok) {
-      my_lse2 = lse[((int64_t)b * Hq + hq) * N + my_q] * kLog2e;
-      my_dlt = delta[((int64_t)b * Hq + hq) * N + my_q];
-    }
+    my_lse2 = lse[((int64_t)b * Hq + hq) * N + row] * kLog2e;
+    my_dlt = delta[((int64_t)b * Hq + hq) * N + row];
   }
 
   int kv_end = N;
@@ -335,17 +338,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   u32x4 kreg[G_PER_T][4], vreg[G_PER_T][4];
   auto load_tile = [&](int t) {
     const int k0 = t * BN;
+    // Key rows past N are read as row N-1; their probabilities are masked to 0.
 #pragma unroll
     for (int r = 0; r < G_PER_T; ++r) {
       const int g = tid + r * kBwdThreads;
       const int dc = g % C8, kg = g / C8;
+      if (GROUPS % kBwdThreads == 0 || g < GROUPS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kg * 4 + i;
-        const bool ok = g < GROUPS && key < N;
-        const int64_t off = (int64_t)key * kv_rs + dc * 8;
-        kreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(kb + off) : u32x4{0, 0, 0, 0};
-        vreg[r][i] = ok ? *reinterpret_cast<const u32x4*>(vb + off) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(k0 + kg * 4 + i, N - 1);
+          const int64_t off = (int64_t)key * kv_rs + dc * 8;
+          kreg[r][i] = *reinterpret_cast<const u32x4*>(kb + off);
+          vreg[r][i] = *reinterpret_cast<const u32x4*>(vb + off);
+        }
       }
     }
   };

@@ -89,13 +89,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 
   constexpr int ROWS_PER_ITER = kDecWaves * RPW * kDecUnroll;
   u32x4 kr[kDecUnroll], vr[kDecUnroll];
+  // Rows past the chunk end are read as the chunk's last row (never past
+  // L_b - 1); their scores are masked to -inf, so they weigh exactly 0.
   auto load = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const int row = base + u * kDecWaves * RPW + state;
-      const bool ok = row < end;
-      kr[u] = ok ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)row * row_stride) : u32x4{0, 0, 0, 0};
-      vr[u] = ok ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)row * row_stride) : u32x4{0, 0, 0, 0};
+      const int row = min(base + u * kDecWaves * RPW + state, end - 1);
+      kr[u] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)row * row_stride);
+      vr[u] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)row * row_stride);
     }
   };
 

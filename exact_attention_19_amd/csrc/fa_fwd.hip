@@ -26,6 +26,9 @@ namespace fa {
 namespace {
 
 constexpr int kBN = 64;  // keys per tile
+// The running maximum used as the exponent reference is only raised when a
+// row's new maximum exceeds it by more than this many powers of two.
+constexpr float kRescaleSlack = 8.f;
 
 template <int D, int NWAVES>
 struct FwdSmem {
@@ -78,14 +81,14 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
   const bool wave_active = qw0 < N;
 
   // Q fragments: B operand of S^T = K Q^T. Lane holds Q[my_q][16 s + 8 hh .. +7].
+  // Rows past N read row N-1 instead (their results are never written), so
+  // no load is predicated.
   bf16x8 qf[DS];
   {
-    const bool ok = my_q < N;
-    const __bf16* qrow = qb + (int64_t)(ok ? my_q : 0) * q_row_stride + 8 * hh;
+    const __bf16* qrow = qb + (int64_t)min(my_q, N - 1) * q_row_stride + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qrow + 16 * s) : u32x4{0, 0, 0, 0};
-      qf[s] = __builtin_bit_cast(bf16x8, w);
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
     }
   }
 
@@ -101,27 +104,28 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
   u32x4 kreg[K_PER_T];
   u32x4 vreg[V_PER_T][4];
 
+  // Key rows past N are read as row N-1: their scores are masked to -inf and
+  // their probabilities are exactly 0, so the duplicate values never count.
   auto load_tile = [&](int t) {
     const int k0 = t * kBN;
 #pragma unroll
     for (int r = 0; r < K_PER_T; ++r) {
       const int c = tid + r * NT;
       const int row = c / C8, col = c % C8;
-      const int key = k0 + row;
-      kreg[r] = (c < K_CHUNKS && key < N)
-                    ? *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kv_row_stride + col * 8)
-                    : u32x4{0, 0, 0, 0};
+      const int key = min(k0 + row, N - 1);
+      if (K_CHUNKS % NT == 0 || c < K_CHUNKS)
+        kreg[r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kv_row_stride + col * 8);
     }
 #pragma unroll
     for (int r = 0; r < V_PER_T; ++r) {
       const int g = tid + r * NT;
       const int dc = g % C8, kg = g / C8;
+      if (V_GROUPS % NT == 0 || g < V_GROUPS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kg * 4 + i;
-        vreg[r][i] = (g < V_GROUPS && key < N)
-                         ? *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kv_row_stride + dc * 8)
-                         : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(k0 + kg * 4 + i, N - 1);
+          vreg[r][i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kv_row_stride + dc * 8);
+        }
       }
     }
   };
@@ -178,45 +182,52 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
           sacc[kbk] = mfma32(a, qf[s], sacc[kbk]);
         }
       }
-      // Scale to log2 units and mask.
+      // Row maximum of the raw (unscaled) scores; masked entries are -inf.
       const bool need_mask = (CAUSAL && (k0 + kBN - 1 > qw0)) || (k0 + kBN > N);
       float mt = kNegInf;
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          float x = sacc[kbk][e] * scale_log2;
+          float x = sacc[kbk][e];
           if (need_mask) {
             const int key = k0 + kbk * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
             const bool masked = (key >= N) || (CAUSAL && key > my_q);
             x = masked ? kNegInf : x;
+            sacc[kbk][e] = x;
           }
-          sacc[kbk][e] = x;
           mt = fmaxf(mt, x);
         }
       }
-      mt = fmaxf(mt, swap_halves(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
+      mt = fmaxf(mt, swap_halves(mt)) * scale_log2;  // log2 units (scale > 0)
+      // Lazy rescale: the reference maximum m_run only moves when some row's
+      // maximum exceeds it by more than kRescaleSlack, so p <= 2^kRescaleSlack.
+      // O and l always share the same reference, so the result is unchanged;
+      // most tiles skip the O *= alpha pass entirely.
+      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+        }
+      }
+      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
       float psum = 0.f;
       bf16x8 pb[4];
 #pragma unroll
       for (int kbk = 0; kbk < 2; ++kbk) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(sacc[kbk][e] - m_use);
+          const float p = fast_exp2(fmaf(sacc[kbk][e], scale_log2, neg_m));
           psum += p;
           pb[kbk * 2 + (e >> 3)][e & 7] = (__bf16)p;
         }
       }
-      l_run = l_run * alpha + psum;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      }
+      l_run += psum;
       // O^T += V^T P^T.
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
