@@ -139,4 +139,65 @@ __device__ __forceinline__ bf16x8 load_tr_operand(const __bf16* tr, int d, int s
   return *reinterpret_cast<const bf16x8*>(tr + d * 64 + u * 8);
 }
 
+// ---------------------------------------------------------------------------
+// Row-major 64 x 128 bf16 tiles in LDS (256 bytes per row), filled straight
+// from global memory with global_load_lds_dwordx4: one wave instruction
+// writes 1 KB (4 rows) contiguously, lane i landing at byte 16 i. The 16-byte
+// units of row r are stored XOR-permuted by tile_swz(r), which is free of
+// LDS bank conflicts both for 16-byte MFMA operand reads down 16 consecutive
+// rows and for ds_read_b64_tr_b16 transposed reads of 4-row x 32-byte blocks
+// (measured on gfx950).
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+
+__device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// DMA rows [row0, row0 + 64) of a [rows][128] bf16 matrix (row stride
+// `stride_bytes`) into a swizzled LDS tile. The calling wave issues chunks
+// c = first + i * step (4 rows each, i < NCHUNK); first and step are
+// wave-uniform and `first % 4 == (first + i * step) % 4` must hold (step a
+// multiple of 4), so the XOR pattern of a lane is the same for every chunk.
+// Rows past `nrows` (the number of valid rows from row0) re-read row
+// nrows - 1 of the tile.
+// Wave-uniform pointer, made explicit so that address arithmetic on it stays
+// in scalar registers.
+__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const unsigned char*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int NCHUNK>
+__device__ __forceinline__ void dma_tile_d128(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
+                                              unsigned char* lds_tile, int first, int step, int lane) {
+  const int lr = lane >> 4;
+  const uint32_t unit_off = 16u * (uint32_t)((lane & 15) ^ tile_swz(4 * first + lr));
+  if (nrows >= 64) {
+    const uint32_t lane_off = (uint32_t)lr * stride_bytes + unit_off;
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      const int c = first + i * step;
+      const unsigned char* cb = uniform_ptr(tile_base + (size_t)(4u * c) * stride_bytes);
+      __builtin_amdgcn_global_load_lds(cb + lane_off, (lds_void*)(lds_tile + c * 1024), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NCHUNK; ++i) {
+      const int c = first + i * step;
+      const uint32_t r = (uint32_t)min(4 * c + lr, nrows - 1);
+      const unsigned char* tb = uniform_ptr(tile_base);
+      __builtin_amdgcn_global_load_lds(tb + (r * stride_bytes + unit_off), (lds_void*)(lds_tile + c * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Transposed read of 4 consecutive rows x 1 column per lane from a swizzled
+// d=128 tile: within each group of 16 lanes, lane j addresses row
+// r0 + j/4, columns 16*cg + 4*(j%4) .. +3 (cg picks the 16-column half of a
+// 32-column block), and receives the 4 rows of column 16*cg + j.
+__device__ __forceinline__ i16x4 tr_read(const unsigned char* lds_tile_byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_tile_byte_addr);
+}
+
 }  // namespace fa

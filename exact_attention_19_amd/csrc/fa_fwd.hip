@@ -18,6 +18,8 @@
 //   its keys stored in that same order, so the permutation cancels.
 // fp32 path: a plain VALU kernel (one query row per lane), used for fp32
 // inputs, where P must not be rounded.
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -266,6 +268,203 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
   }
 }
 
+// bf16 path for d = 128. K and V tiles go from global memory straight into
+// swizzled row-major LDS tiles (no staging registers, no transposing stores);
+// the V^T operand of the P V product is read with ds_read_b64_tr_b16, whose
+// 4-row blocks are exactly the key groups the score accumulator hands to one
+// 16-key MFMA step: elements 0-3 are keys 16*st + 4*hh + {0..3}, elements
+// 4-7 are keys 16*st + 8 + 4*hh + {0..3}.
+template <int NWAVES, bool CAUSAL>
+__global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
+    int num_q_tiles) {
+  constexpr int D = 128;
+  constexpr int BM = NWAVES * 32;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int TILE = 64 * 256;        // bytes of one 64 x 128 bf16 tile
+  constexpr int STAGE = 2 * TILE;       // K tile then V tile
+  constexpr int CPW = 16 / NWAVES;      // 1 KB chunks per wave per tile
+  extern __shared__ __align__(1024) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+
+  const int BH = B * Hq;
+  const int bid = blockIdx.x;
+  const int bh = bid % BH;
+  const int rank = bid / BH;
+  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const __bf16* kb = k + ((int64_t)b * N) * kv_rs + (int64_t)hk * D;
+  const __bf16* vb = v + ((int64_t)b * N) * kv_rs + (int64_t)hk * D;
+
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+  const bool wave_active = qw0 < N;
+
+  bf16x8 qf[DS];
+  {
+    const __bf16* qrow = q + ((int64_t)b * N + min(my_q, N - 1)) * q_rs + (int64_t)hq * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
+  }
+
+  int kv_end = N;
+  if (CAUSAL) kv_end = min(N, q0 + BM);
+  const int n_tiles = (kv_end + 63) / 64;
+
+  // Per-lane LDS byte offsets inside a tile (constant over the loop).
+  // K operand (A of S^T): row 32*kbk + l32, logical unit 2*s + hh.
+  //   offset = row*256 + 16*((2s + hh) ^ swz(row)) = koff ^ (32*s) + kbk*8192.
+  const int koff = l32 * 256 + 16 * (hh ^ tile_swz(l32));
+  // V^T operand (A of O^T): tr reads at rows 16*st + 4*hh + j/4 (+8), column
+  // block 32*db + 16*(g&1) + 4*(j&3), j = lane & 15, g = lane >> 4.
+  int voff[2];
+  {
+    const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int r = 4 * hh + (j >> 2) + 8 * rd;
+      const int unit = 2 * (g & 1) + ((j & 3) >> 1);  // db = 0
+      voff[rd] = r * 256 + 16 * (unit ^ tile_swz(r)) + 8 * (j & 1);
+    }
+  }
+
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+    unsigned char* st = smem + stage * STAGE;
+    const int64_t off = (int64_t)t * 64 * kv_rs * 2;
+    const int nrows = N - t * 64;
+    dma_tile_d128<CPW>(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, lane);
+    dma_tile_d128<CPW>(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES,
+                       lane);
+  };
+
+  // One 32-key block (keys k0 .. k0+31 of the tile in LDS at ks/vs, block
+  // index kbk): S^T, softmax update, O^T += V^T P^T. Working on 32 keys at a
+  // time keeps the live score and operand registers small.
+  auto block = [&](const unsigned char* ks, const unsigned char* vs, int k0, int kbk, bool need_mask)
+                   __attribute__((always_inline)) {
+    f32x16 sacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (koff ^ (32 * s)));
+      sacc = mfma32(a, qf[s], sacc);
+    }
+    // Element e holds key k0 + 32*kbk + 4*hh + c(e) with c(e) = 8*(e/4) + e%4,
+    // a compile-time constant; it is masked iff c(e) > lim, where lim folds
+    // the causal bound (key <= my_q) and the sequence end (key < N). The
+    // branch is wave-uniform and taken only on diagonal or ragged tiles.
+    if (need_mask) {
+      const int base_key = k0 + kbk * 32 + 4 * hh;
+      int lim = N - 1 - base_key;
+      if (CAUSAL) lim = min(lim, my_q - base_key);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sacc[e];
+    }
+    float mt = sacc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
+    mt = fmaxf(mt, swap_halves(mt)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      }
+    }
+    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+    float psum = 0.f;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float p = fast_exp2(fmaf(sacc[e], scale_log2, neg_m));
+      psum += p;
+      pb[e >> 3][e & 7] = (__bf16)p;
+    }
+    l_run += psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int st = 2 * kbk + tt;
+        const i16x4 lo = tr_read(vs + st * 4096 + (voff[0] ^ (64 * db)));
+        const i16x4 hi = tr_read(vs + st * 4096 + (voff[1] ^ (64 * db)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = mfma32(a, pb[tt], oacc[db]);
+      }
+    }
+  };
+
+  auto tile = [&](const unsigned char* ks, const unsigned char* vs, int k0, bool need_mask)
+                  __attribute__((always_inline)) {
+    block(ks, vs, k0, 0, need_mask);
+    block(ks, vs, k0, 1, need_mask);
+  };
+
+  // One pipeline step on LDS stage STG (a compile-time constant, so every
+  // LDS offset below is an immediate): prefetch tile t+1 into the other
+  // stage, then consume tile t.
+  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
+    const int k0 = t * 64;
+    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    if (!skip) {
+      const unsigned char* ks = smem + STG * STAGE;
+      const bool need_mask = (CAUSAL && (k0 + 63 > qw0)) || (k0 + 64 > N);
+      tile(ks, ks + TILE, k0, need_mask);
+    }
+    __syncthreads();
+  };
+
+  issue(0, 0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!wave_active) return;
+  const float l_tot = l_run + swap_halves(l_run);
+  if (my_q < N) {
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    __bf16* orow = o + ((int64_t)b * N + my_q) * q_rs + (int64_t)hq * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hh) = w;
+      }
+    }
+    if (hh == 0) lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
 // fp32 path: one query row per lane, 32-key tiles staged in LDS.
 template <int D>
 __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(
@@ -352,6 +551,23 @@ hipError_t launch_bf16(const FwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int NWAVES, bool CAUSAL>
+hipError_t launch_d128(const FwdArgs& a) {
+  constexpr int BM = NWAVES * 32;
+  const int num_q_tiles = (a.N + BM - 1) / BM;
+  const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  constexpr size_t smem = 2 * 2 * 64 * 256;
+  auto kern = fwd_d128_kernel<NWAVES, CAUSAL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
+                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
+                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles);
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_f32(const FwdArgs& a) {
   const int num_q_tiles = (a.N + 63) / 64;
@@ -372,7 +588,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   if (a.d == 64) {
     return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
   }
-  return a.causal ? launch_bf16<128, 4, true>(a) : launch_bf16<128, 4, false>(a);
+  return a.causal ? launch_d128<4, true>(a) : launch_d128<4, false>(a);
 }
 
 }  // namespace fa
