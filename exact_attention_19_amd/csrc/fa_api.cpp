@@ -65,7 +65,8 @@ fa_status hip_status(const char* fn, hipError_t e) {
   return ok();
 }
 
-size_t bwd_ws_bytes(int B, int Hq, int N) { return round_up((size_t)B * Hq * N * sizeof(float), 256); }
+// D and LSE * log2(e), each [B, Hq, N] float32.
+size_t bwd_ws_bytes(int B, int Hq, int N) { return 2 * fa::bwd_vec_stride(B, Hq, N) * sizeof(float); }
 
 void decode_ws_layout(int B, int Hq, int N, int d, int num_splits, int* chunk, int* nsplit, size_t* o_bytes,
                       size_t* lse_bytes) {
@@ -84,6 +85,7 @@ fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, co
   if (all || stage == 0) {
     FA_TRY(check_ptr(fn, "o", o, 16));
     FA_TRY(check_ptr(fn, "dout", dout, 16));
+    FA_TRY(check_ptr(fn, "lse", lse, 4));
   }
   if (all || stage >= 1) {
     FA_TRY(check_ptr(fn, "q", q, 16));

@@ -9,7 +9,8 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream:
-//   1. preprocess: D = rowsum(dO * O) per (b, head, row), float32.
+//   1. preprocess: D = rowsum(dO * O) per (b, head, row), float32, and the
+//      logsumexp rescaled to log2 units (LSE * log2 e) for the exp2 below.
 //   2. dK/dV: one workgroup per (b, kv head, 128-key tile). Each wave keeps
 //      32 keys' K and V fragments and their dK^T, dV^T accumulators in
 //      registers and sweeps every query head of the GQA group and every
@@ -20,6 +21,8 @@
 //      the forward (S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T).
 // No atomics: the result is bit-reproducible. dS is recomputed in both
 // kernels (seven tile products per tile pair instead of five).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -34,7 +37,9 @@ constexpr int kBwdThreads = 256;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __restrict__ o,
                                                              const __bf16* __restrict__ dout,
-                                                             float* __restrict__ delta, int B, int Hq, int N) {
+                                                             const float* __restrict__ lse,
+                                                             float* __restrict__ delta, float* __restrict__ lse2,
+                                                             int B, int Hq, int N) {
   constexpr int LPT = D / 8;
   const int64_t rows = (int64_t)B * N * Hq;
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -51,7 +56,9 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
     const int64_t rem = rr - b * per_b;
     const int64_t i = rem / Hq;
     const int64_t h = rem - i * Hq;
-    delta[(b * Hq + h) * N + i] = tot;
+    const int64_t idx = (b * Hq + h) * N + i;
+    delta[idx] = tot;
+    lse2[idx] = lse[idx] * kLog2e;  // exponent reference in log2 units
   }
 }
 
@@ -437,6 +444,333 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// d = 128 kernels. Row-major 64 x 128 tiles go from global memory straight
+// into XOR-swizzled LDS (global_load_lds_dwordx4); transposed MFMA operands
+// (Q^T, dO^T, K^T) are read from the same tiles with ds_read_b64_tr_b16, so
+// no tile is stored twice and nothing passes through staging registers.
+// For a 16-row step st of a 64-row tile, a transposed read at row offset
+// 4*hh + j/4 (+8) yields, for the lane's column, the rows the score
+// accumulator pairs with it: 16*st + 4*hh + {0..3} and 16*st + 8 + 4*hh + {0..3}.
+
+// Per-lane byte offsets inside a swizzled tile for a transposed operand read
+// (second read at index 1), for column block 0; column block db is reached by
+// XOR with 64*db, 16-row step st by adding 4096*st.
+__device__ __forceinline__ void tr_offsets(int lane, int (&off)[2]) {
+  const int j = lane & 15, g = lane >> 4, hh = lane >> 5;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int r = 4 * hh + (j >> 2) + 8 * rd;
+    const int unit = 2 * (g & 1) + ((j & 3) >> 1);
+    off[rd] = r * 256 + 16 * (unit ^ tile_swz(r)) + 8 * (j & 1);
+  }
+}
+
+__device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int st, int db, const int (&off)[2]) {
+  const i16x4 lo = tr_read(tile + st * 4096 + (off[0] ^ (64 * db)));
+  const i16x4 hi = tr_read(tile + st * 4096 + (off[1] ^ (64 * db)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Row operand (16 bytes of row r0 + l32, 16-deep step s) from a swizzled
+// tile: byte offset (roff ^ (32*s)) + 8192 * (r0 / 32), roff from row_offset.
+__device__ __forceinline__ int row_offset(int lane) {
+  const int l32 = lane & 31, hh = lane >> 5;
+  return l32 * 256 + 16 * (hh ^ tile_swz(l32));
+}
+
+// dK, dV for d = 128: one workgroup per (b, kv head, 128 keys); wave w keeps
+// keys k0 + 32w .. +31 (K, V fragments and dK^T, dV^T accumulators in
+// registers) and sweeps the visible 64-row query tiles of every query head
+// in the GQA group.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
+    float scale_log2) {
+  constexpr int D = 128, DS = 8, DB = 4, BQ = 64, BKV = 128;
+  constexpr int TILE = 64 * 256;
+  constexpr int VEC_OFF = 2 * TILE;            // lse2 (64 floats) then delta (64 floats)
+  constexpr int STAGE = 2 * TILE + 512;
+  extern __shared__ __align__(1024) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int BHK = B * Hkv;
+  const int bhk = blockIdx.x % BHK;
+  const int kt = blockIdx.x / BHK;
+  const int b = bhk / Hkv;
+  const int hk = bhk - b * Hkv;
+  const int G = Hq / Hkv;
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;
+  const bool wave_active = kw0 < N;
+
+  bf16x8 kf[DS], vf[DS];
+  {
+    const int64_t off = ((int64_t)b * N + min(my_key, N - 1)) * kv_rs + (int64_t)hk * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k + off + 16 * s));
+      vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(v + off + 16 * s));
+    }
+  }
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
+  const int per_head = nqt - qt0;
+  const int n_iter = G * per_head;
+
+  const int roff = row_offset(lane);
+  int toff[2];
+  tr_offsets(lane, toff);
+  const uint32_t q_rs_bytes = (uint32_t)(q_rs * 2);
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+
+  auto issue = [&](int it, int stage) __attribute__((always_inline)) {
+    const int hq = hk * G + it / per_head;
+    const int q0 = (qt0 + it % per_head) * BQ;
+    unsigned char* st = smem + stage * STAGE;
+    const int64_t off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
+    dma_tile_d128<4>(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, 4, lane);
+    dma_tile_d128<4>(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave, 4,
+                     lane);
+    const int64_t vb = ((int64_t)b * Hq + hq) * N;
+    if (wave == 0) dma_vec64_f32(lse2 + vb, q0, N - 1, st + VEC_OFF, lane);
+    if (wave == 1) dma_vec64_f32(delta + vb, q0, N - 1, st + VEC_OFF + 256, lane);
+  };
+
+  // One 32-query block qb of the tile in stage memory `st`.
+  auto block = [&](const unsigned char* st, int q0, int qb, bool need_mask) __attribute__((always_inline)) {
+    const unsigned char* qs = st;
+    const unsigned char* ds_ = st + TILE;
+    const float* lse_s = reinterpret_cast<const float*>(st + VEC_OFF);
+    const float* dlt_s = lse_s + 64;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      sacc = mfma32(*reinterpret_cast<const bf16x8*>(qs + qb * 8192 + (roff ^ (32 * s))), kf[s], sacc);
+      dpacc = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + qb * 8192 + (roff ^ (32 * s))), vf[s], dpacc);
+    }
+    // Element e is query q0 + 32*qb + 4*hh + c(e), c(e) = 8*(e/4) + e%4. It is
+    // masked when the query precedes the key (causal) or is past N.
+    int lo = -1, hi = 1 << 30;
+    if (need_mask) {
+      const int qbase = q0 + 32 * qb + 4 * hh;
+      if (CAUSAL) lo = my_key - qbase - 1;  // masked iff c(e) <= lo
+      hi = N - qbase;                        // masked iff c(e) >= hi
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * qb + 8 * jj + 4 * hh);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_s + 32 * qb + 8 * jj + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * jj + i;
+        float p = fast_exp2(fmaf(sacc[e], scale_log2, -l4[i]));
+        if (need_mask) {
+          const int c = 8 * jj + i;
+          p = (c <= lo || c >= hi) ? 0.f : p;
+        }
+        pb[e >> 3][e & 7] = (__bf16)p;
+        dsb[e >> 3][e & 7] = (__bf16)(p * (dpacc[e] - d4[i]));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int stp = 2 * qb + tt;
+        dvacc[db] = mfma32(tr_operand(ds_, stp, db, toff), pb[tt], dvacc[db]);
+        dkacc[db] = mfma32(tr_operand(qs, stp, db, toff), dsb[tt], dkacc[db]);
+      }
+    }
+  };
+
+  auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (it + 1 < n_iter) issue(it + 1, STG ^ 1);
+    const int q0 = (qt0 + it % per_head) * BQ;
+    const bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
+    if (!skip) {
+      const unsigned char* st = smem + STG * STAGE;
+      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
+      block(st, q0, 0, need_mask);
+      block(st, q0, 1, need_mask);
+    }
+    __syncthreads();
+  };
+
+  if (n_iter > 0) issue(0, 0);
+  __syncthreads();
+  for (int it = 0; it < n_iter; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < n_iter) step(it + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!wave_active || my_key >= N) return;
+  const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = db * 32 + 8 * j + 4 * hh;
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2(dkacc[db][4 * j + 0] * scale, dkacc[db][4 * j + 1] * scale);
+      wk[1] = pack_bf16x2(dkacc[db][4 * j + 2] * scale, dkacc[db][4 * j + 3] * scale);
+      wv[0] = pack_bf16x2(dvacc[db][4 * j + 0], dvacc[db][4 * j + 1]);
+      wv[1] = pack_bf16x2(dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]);
+      *reinterpret_cast<u32x2*>(dk + off + d) = wk;
+      *reinterpret_cast<u32x2*>(dv + off + d) = wv;
+    }
+  }
+}
+
+// dQ for d = 128: one workgroup per (b, query head, 128 query rows), shaped
+// like the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+template <bool CAUSAL>
+__global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles) {
+  constexpr int D = 128, DS = 8, DB = 4, BM = 128, BN = 64;
+  constexpr int TILE = 64 * 256;
+  constexpr int STAGE = 2 * TILE;  // K tile then V tile
+  extern __shared__ __align__(1024) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int BH = B * Hq;
+  const int bh = blockIdx.x % BH;
+  const int rank = blockIdx.x / BH;
+  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
+  const int b = bh / Hq;
+  const int hq = bh - b * Hq;
+  const int hk = hq / (Hq / Hkv);
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const int q0 = qt * BM;
+  const int qw0 = q0 + wave * 32;
+  const int my_q = qw0 + l32;
+  const bool wave_active = qw0 < N;
+
+  bf16x8 qf[DS], dof[DS];
+  float my_lse2, my_dlt;
+  {
+    const int row = min(my_q, N - 1);
+    const int64_t off = ((int64_t)b * N + row) * q_rs + (int64_t)hq * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off + 16 * s));
+      dof[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dout + off + 16 * s));
+    }
+    my_lse2 = lse2[((int64_t)b * Hq + hq) * N + row];
+    my_dlt = delta[((int64_t)b * Hq + hq) * N + row];
+  }
+
+  int kv_end = N;
+  if (CAUSAL) kv_end = min(N, q0 + BM);
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k + (int64_t)b * N * kv_rs + (int64_t)hk * D);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v + (int64_t)b * N * kv_rs + (int64_t)hk * D);
+  const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+
+  const int roff = row_offset(lane);
+  int toff[2];
+  tr_offsets(lane, toff);
+
+  f32x16 dqacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
+
+  auto issue = [&](int t, int stage) __attribute__((always_inline)) {
+    unsigned char* st = smem + stage * STAGE;
+    const int64_t off = (int64_t)t * BN * kv_rs * 2;
+    dma_tile_d128<4>(kbase + off, kv_rs_bytes, N - t * BN, st, wave, 4, lane);
+    dma_tile_d128<4>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, lane);
+  };
+
+  auto block = [&](const unsigned char* st, int k0, int kbk, bool need_mask) __attribute__((always_inline)) {
+    const unsigned char* ks = st;
+    const unsigned char* vs = st + TILE;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      sacc = mfma32(*reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (roff ^ (32 * s))), qf[s], sacc);
+      dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vs + kbk * 8192 + (roff ^ (32 * s))), dof[s], dpacc);
+    }
+    // Element e is key k0 + 32*kbk + 4*hh + c(e), c(e) = 8*(e/4) + e%4.
+    int lim = 1 << 30;
+    if (need_mask) {
+      const int base_key = k0 + kbk * 32 + 4 * hh;
+      lim = N - 1 - base_key;
+      if (CAUSAL) lim = min(lim, my_q - base_key);
+    }
+    bf16x8 dsb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = fast_exp2(fmaf(sacc[e], scale_log2, -my_lse2));
+      if (need_mask) p = (8 * (e >> 2) + (e & 3) > lim) ? 0.f : p;
+      dsb[e >> 3][e & 7] = (__bf16)(p * (dpacc[e] - my_dlt));
+    }
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        dqacc[db] = mfma32(tr_operand(ks, 2 * kbk + tt, db, toff), dsb[tt], dqacc[db]);
+      }
+    }
+  };
+
+  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+    constexpr int STG = decltype(stage_tag)::value;
+    if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
+    const int k0 = t * BN;
+    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    if (!skip) {
+      const unsigned char* st = smem + STG * STAGE;
+      const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw0)) || (k0 + BN > N);
+      block(st, k0, 0, need_mask);
+      block(st, k0, 1, need_mask);
+    }
+    __syncthreads();
+  };
+
+  issue(0, 0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+  }
+
+  if (!wave_active || my_q >= N) return;
+  __bf16* orow = dq + ((int64_t)b * N + my_q) * q_rs + (int64_t)hq * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w[0] = pack_bf16x2(dqacc[db][4 * j + 0] * scale, dqacc[db][4 * j + 1] * scale);
+      w[1] = pack_bf16x2(dqacc[db][4 * j + 2] * scale, dqacc[db][4 * j + 3] * scale);
+      *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hh) = w;
+    }
+  }
+}
+
 template <typename K>
 hipError_t set_smem(K kern, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -446,18 +780,30 @@ hipError_t set_smem(K kern, size_t bytes) {
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const float scale_log2 = a.scale * kLog2e;
+  float* lse2 = delta + bwd_vec_stride(a.B, a.Hq, a.N);
   if (stage == 0) {
     const int64_t threads = (int64_t)a.B * a.N * a.Hq * (D / 8);
     const int64_t grid = (threads + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)grid), dim3(256), 0, a.stream,
-                       (const __bf16*)a.o, (const __bf16*)a.dout, delta, a.B, a.Hq, a.N);
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, delta, lse2, a.B, a.Hq, a.N);
     return hipGetLastError();
   }
   if (stage == 1) {
     const int nkt = (a.N + 127) / 128;
     const int64_t grid = (int64_t)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (D == 128) {
+      auto kern = bwd_dkdv_d128_kernel<CAUSAL>;
+      constexpr size_t smem = 2 * (2 * 64 * 256 + 512);
+      hipError_t e = set_smem(kern, smem);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
+                         (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
+                         (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
+                         scale_log2);
+      return hipGetLastError();
+    }
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
     hipError_t e = set_smem(kern, DkdvSmem<D>::BYTES);
     if (e != hipSuccess) return e;
@@ -470,6 +816,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const int nqt = (a.N + 127) / 128;
   const int64_t grid = (int64_t)nqt * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (D == 128) {
+    auto kern = bwd_dq_d128_kernel<CAUSAL>;
+    constexpr size_t smem = 2 * 2 * 64 * 256;
+    hipError_t e = set_smem(kern, smem);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
+                       (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
+                       (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
+    return hipGetLastError();
+  }
   auto kern = bwd_dq_kernel<D, CAUSAL>;
   hipError_t e = set_smem(kern, DqSmem<D>::BYTES);
   if (e != hipSuccess) return e;

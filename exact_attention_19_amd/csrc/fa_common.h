@@ -192,6 +192,14 @@ __device__ __forceinline__ void dma_tile_d128(const unsigned char* tile_base, ui
   }
 }
 
+// DMA 64 consecutive floats src[i0 + lane] (indices clamped to `last`) into
+// LDS dst[lane]: one wave instruction.
+__device__ __forceinline__ void dma_vec64_f32(const float* src, int i0, int last, unsigned char* lds_dst, int lane) {
+  const unsigned char* base = uniform_ptr(reinterpret_cast<const unsigned char*>(src));
+  const uint32_t idx = (uint32_t)min(i0 + lane, last);
+  __builtin_amdgcn_global_load_lds(base + 4u * idx, (lds_void*)lds_dst, 4, 0, 0);
+}
+
 // Transposed read of 4 consecutive rows x 1 column per lane from a swizzled
 // d=128 tile: within each group of 16 lanes, lane j addresses row
 // r0 + j/4, columns 16*cg + 4*(j%4) .. +3 (cg picks the 16-column half of a

@@ -58,8 +58,12 @@ constexpr int kDecodeMaxHeadsPerGroup = 4;
 
 hipError_t launch_fwd(const FwdArgs& a);
 
-// Backward: D = rowsum(dO * O) is written to `delta` ([B, Hq, N] float32).
-// Stage 0 computes D, stage 1 dK and dV, stage 2 dQ; launch_bwd runs all three.
+// Backward workspace: D = rowsum(dO * O) at `delta` ([B, Hq, N] float32),
+// then LSE * log2(e) at delta + bwd_vec_stride(...) (same shape).
+// Stage 0 computes both, stage 1 dK and dV, stage 2 dQ; launch_bwd runs all three.
+inline size_t bwd_vec_stride(int B, int Hq, int N) {
+  return ((size_t)B * Hq * N + 63) / 64 * 64;  // floats; keeps the second vector 256-byte aligned
+}
 hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage);
 hipError_t launch_bwd(const BwdArgs& a, float* delta);
 

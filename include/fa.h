@@ -95,10 +95,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 /*
  * One stage of fa_bwd, for callers that schedule or time the stages
  * separately. fa_bwd is exactly stage 0, then 1, then 2 on one stream, with
- * the same arguments and workspace (stage 0 writes D = rowsum(dO * O) into
- * the workspace, stages 1 and 2 read it):
+ * the same arguments and workspace (stage 0 writes D = rowsum(dO * O) and the
+ * logsumexp in log2 units into the workspace, stages 1 and 2 read them):
  *   stage 0: D;  stage 1: dK and dV;  stage 2: dQ.
- * Pointers a stage does not use may be NULL (stage 0 reads only o, dout;
+ * Pointers a stage does not use may be NULL (stage 0 reads only o, dout, lse;
  * stage 1 writes only dk, dv; stage 2 writes only dq). Any other stage
  * number returns FA_ERR_INVALID_ARG.
  */

@@ -105,7 +105,7 @@ def test_decode_validation(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.fa_bwd_workspace_bytes(1, 96, 96, 8192, 128) == 96 * 8192 * 4
+    assert lib.fa_bwd_workspace_bytes(1, 96, 96, 8192, 128) == 2 * 96 * 8192 * 4  # D and LSE*log2(e)
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 1, 64) == 0
     # default split: 512-row chunks -> 64 splits for a 32768-row cache
     o_bytes = 64 * 32 * 64 * 128 * 4
