@@ -550,27 +550,44 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     if (wave == 1) dma_vec64_f32(delta + vb, q0, N - 1, st + VEC_OFF + 256, lane);
   };
 
-  // One 32-query block qb of the tile in stage memory `st`.
-  auto block = [&](const unsigned char* st, int q0, int qb, bool need_mask) __attribute__((always_inline)) {
+  // The tile's two 32-query blocks are skewed so that independent work sits
+  // side by side for the scheduler: S/dP of block 1 next to the softmax
+  // algebra of block 0, and the dV/dK products of block 0 next to the
+  // algebra of block 1.
+  //   scores(qb):  S = Q K^T and dP = dO V^T for the 32 queries of block qb
+  //   algebra(qb): P = exp2(S*c - LSE2), dS = P * (dP - D), both to bf16
+  //   update(qb):  dV^T += dO^T P, dK^T += Q^T dS
+  struct Scores { f32x16 s, dp; };
+  struct Probs { bf16x8 p[2], ds[2]; };
+  auto scores = [&](const unsigned char* st, int qb) __attribute__((always_inline)) {
     const unsigned char* qs = st;
     const unsigned char* ds_ = st + TILE;
-    const float* lse_s = reinterpret_cast<const float*>(st + VEC_OFF);
-    const float* dlt_s = lse_s + 64;
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    Scores r{f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      sacc = mfma32(*reinterpret_cast<const bf16x8*>(qs + qb * 8192 + (roff ^ (32 * s))), kf[s], sacc);
-      dpacc = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + qb * 8192 + (roff ^ (32 * s))), vf[s], dpacc);
+      r.s = mfma32(*reinterpret_cast<const bf16x8*>(qs + qb * 8192 + (roff ^ (32 * s))), kf[s], r.s);
+      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + qb * 8192 + (roff ^ (32 * s))), vf[s], r.dp);
     }
-    // Element e is query q0 + 32*qb + 4*hh + c(e), c(e) = 8*(e/4) + e%4. It is
-    // masked when the query precedes the key (causal) or is past N.
-    int lo = -1, hi = 1 << 30;
-    if (need_mask) {
-      const int qbase = q0 + 32 * qb + 4 * hh;
-      if (CAUSAL) lo = my_key - qbase - 1;  // masked iff c(e) <= lo
-      hi = N - qbase;                        // masked iff c(e) >= hi
+    return r;
+  };
+  // Element e of a block is query q0 + 32*qb + 4*hh + c(e), c(e) = 8*(e/4) +
+  // e%4. It is masked (score set to -inf, so P = dS = 0) when the query
+  // precedes the key (causal) or lies past N. Called under a wave-uniform
+  // branch on diagonal and ragged tiles only.
+  auto apply_mask = [&](Scores& sc, int q0, int qb) __attribute__((always_inline)) {
+    const int qbase = q0 + 32 * qb + 4 * hh;
+    const int lo = CAUSAL ? my_key - qbase - 1 : -1;  // masked iff c(e) <= lo
+    const int hi = N - qbase;                          // masked iff c(e) >= hi
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 8 * (e >> 2) + (e & 3);
+      sc.s[e] = (c <= lo || c >= hi) ? kNegInf : sc.s[e];
     }
-    bf16x8 pb[2], dsb[2];
+  };
+  auto algebra = [&](const unsigned char* st, int qb, const Scores& sc) __attribute__((always_inline)) {
+    const float* lse_s = reinterpret_cast<const float*>(st + VEC_OFF);
+    const float* dlt_s = lse_s + 64;
+    Probs r;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * qb + 8 * jj + 4 * hh);
@@ -578,24 +595,35 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int e = 4 * jj + i;
-        float p = fast_exp2(fmaf(sacc[e], scale_log2, -l4[i]));
-        if (need_mask) {
-          const int c = 8 * jj + i;
-          p = (c <= lo || c >= hi) ? 0.f : p;
-        }
-        pb[e >> 3][e & 7] = (__bf16)p;
-        dsb[e >> 3][e & 7] = (__bf16)(p * (dpacc[e] - d4[i]));
+        const float p = fast_exp2(fmaf(sc.s[e], scale_log2, -l4[i]));
+        r.p[e >> 3][e & 7] = (__bf16)p;
+        r.ds[e >> 3][e & 7] = (__bf16)(p * (sc.dp[e] - d4[i]));
       }
     }
+    return r;
+  };
+  auto update = [&](const unsigned char* st, int qb, const Probs& pr) __attribute__((always_inline)) {
+    const unsigned char* qs = st;
+    const unsigned char* ds_ = st + TILE;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int stp = 2 * qb + tt;
-        dvacc[db] = mfma32(tr_operand(ds_, stp, db, toff), pb[tt], dvacc[db]);
-        dkacc[db] = mfma32(tr_operand(qs, stp, db, toff), dsb[tt], dkacc[db]);
+        dvacc[db] = mfma32(tr_operand(ds_, stp, db, toff), pr.p[tt], dvacc[db]);
+        dkacc[db] = mfma32(tr_operand(qs, stp, db, toff), pr.ds[tt], dkacc[db]);
       }
     }
+  };
+  auto tile_body = [&](const unsigned char* st, int q0, bool need_mask) __attribute__((always_inline)) {
+    Scores s0 = scores(st, 0);
+    if (need_mask) apply_mask(s0, q0, 0);
+    Scores s1 = scores(st, 1);
+    const Probs p0 = algebra(st, 0, s0);
+    if (need_mask) apply_mask(s1, q0, 1);
+    update(st, 0, p0);
+    const Probs p1 = algebra(st, 1, s1);
+    update(st, 1, p1);
   };
 
   auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
@@ -606,8 +634,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     if (!skip) {
       const unsigned char* st = smem + STG * STAGE;
       const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
-      block(st, q0, 0, need_mask);
-      block(st, q0, 1, need_mask);
+      tile_body(st, q0, need_mask);
     }
     __syncthreads();
   };
