@@ -731,36 +731,57 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     dma_tile_d128<4>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, lane);
   };
 
-  auto block = [&](const unsigned char* st, int k0, int kbk, bool need_mask) __attribute__((always_inline)) {
+  // Same skew as the dK/dV kernel: scores of key block 1 beside the algebra
+  // of block 0, the dQ product of block 0 beside the algebra of block 1.
+  struct Scores { f32x16 s, dp; };
+  auto scores = [&](const unsigned char* st, int kbk) __attribute__((always_inline)) {
     const unsigned char* ks = st;
     const unsigned char* vs = st + TILE;
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
+    Scores r{f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      sacc = mfma32(*reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (roff ^ (32 * s))), qf[s], sacc);
-      dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vs + kbk * 8192 + (roff ^ (32 * s))), dof[s], dpacc);
+      r.s = mfma32(*reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (roff ^ (32 * s))), qf[s], r.s);
+      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(vs + kbk * 8192 + (roff ^ (32 * s))), dof[s], r.dp);
     }
-    // Element e is key k0 + 32*kbk + 4*hh + c(e), c(e) = 8*(e/4) + e%4.
-    int lim = 1 << 30;
-    if (need_mask) {
-      const int base_key = k0 + kbk * 32 + 4 * hh;
-      lim = N - 1 - base_key;
-      if (CAUSAL) lim = min(lim, my_q - base_key);
-    }
-    bf16x8 dsb[2];
+    return r;
+  };
+  // Element e is key k0 + 32*kbk + 4*hh + c(e), c(e) = 8*(e/4) + e%4; masked
+  // keys (past the causal bound or past N) get score -inf.
+  auto apply_mask = [&](Scores& sc, int k0, int kbk) __attribute__((always_inline)) {
+    const int base_key = k0 + kbk * 32 + 4 * hh;
+    int lim = N - 1 - base_key;
+    if (CAUSAL) lim = min(lim, my_q - base_key);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc.s[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc.s[e];
+  };
+  struct DsB { bf16x8 v[2]; };
+  auto algebra = [&](const Scores& sc) __attribute__((always_inline)) {
+    DsB r;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float p = fast_exp2(fmaf(sacc[e], scale_log2, -my_lse2));
-      if (need_mask) p = (8 * (e >> 2) + (e & 3) > lim) ? 0.f : p;
-      dsb[e >> 3][e & 7] = (__bf16)(p * (dpacc[e] - my_dlt));
+      const float p = fast_exp2(fmaf(sc.s[e], scale_log2, -my_lse2));
+      r.v[e >> 3][e & 7] = (__bf16)(p * (sc.dp[e] - my_dlt));
     }
+    return r;
+  };
+  auto update = [&](const unsigned char* st, int kbk, const DsB& d) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        dqacc[db] = mfma32(tr_operand(ks, 2 * kbk + tt, db, toff), dsb[tt], dqacc[db]);
+        dqacc[db] = mfma32(tr_operand(st, 2 * kbk + tt, db, toff), d.v[tt], dqacc[db]);
       }
     }
+  };
+  auto tile_body = [&](const unsigned char* st, int k0, bool need_mask) __attribute__((always_inline)) {
+    Scores s0 = scores(st, 0);
+    if (need_mask) apply_mask(s0, k0, 0);
+    Scores s1 = scores(st, 1);
+    const DsB d0 = algebra(s0);
+    if (need_mask) apply_mask(s1, k0, 1);
+    update(st, 0, d0);
+    const DsB d1 = algebra(s1);
+    update(st, 1, d1);
   };
 
   auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
@@ -771,8 +792,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     if (!skip) {
       const unsigned char* st = smem + STG * STAGE;
       const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw0)) || (k0 + BN > N);
-      block(st, k0, 0, need_mask);
-      block(st, k0, 1, need_mask);
+      tile_body(st, k0, need_mask);
     }
     __syncthreads();
   };
