@@ -502,8 +502,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   const int BHK = B * Hkv;
   const int bhk = blockIdx.x % BHK;
   const int kt = blockIdx.x / BHK;
-  const int b = bhk / Hkv;
-  const int hk = bhk - b * Hkv;
+  const int b = uniform(bhk / Hkv);
+  const int hk = uniform(bhk - b * Hkv);
   const int G = Hq / Hkv;
 
   const int64_t q_rs = (int64_t)Hq * D;
@@ -532,6 +532,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   int toff[2];
   tr_offsets(lane, toff);
   const uint32_t q_rs_bytes = (uint32_t)(q_rs * 2);
+  const uint32_t dma_off = dma_lane_offset(lane, wave, q_rs_bytes);
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -542,9 +543,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     const int q0 = (qt0 + it % per_head) * BQ;
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
-    dma_tile_d128<4>(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, 4, lane);
-    dma_tile_d128<4>(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave, 4,
-                     lane);
+    dma_tile_d128<4, 4>(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, dma_off);
+    dma_tile_d128<4, 4>(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave,
+                        dma_off);
     const int64_t vb = ((int64_t)b * Hq + hq) * N;
     if (wave == 0) dma_vec64_f32(lse2 + vb, q0, N - 1, st + VEC_OFF, lane);
     if (wave == 1) dma_vec64_f32(delta + vb, q0, N - 1, st + VEC_OFF + 256, lane);
@@ -684,9 +685,9 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   const int bh = blockIdx.x % BH;
   const int rank = blockIdx.x / BH;
   const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
+  const int b = uniform(bh / Hq);
+  const int hq = uniform(bh - b * Hq);
+  const int hk = uniform(hq / (Hq / Hkv));
 
   const int64_t q_rs = (int64_t)Hq * D;
   const int64_t kv_rs = (int64_t)Hkv * D;
@@ -715,6 +716,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+  const uint32_t dma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
 
   const int roff = row_offset(lane);
   int toff[2];
@@ -727,8 +729,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * BN * kv_rs * 2;
-    dma_tile_d128<4>(kbase + off, kv_rs_bytes, N - t * BN, st, wave, 4, lane);
-    dma_tile_d128<4>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, lane);
+    dma_tile_d128<4, 4>(kbase + off, kv_rs_bytes, N - t * BN, st, wave, dma_off);
+    dma_tile_d128<4, 4>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, dma_off);
   };
 
   // Same skew as the dK/dV kernel: scores of key block 1 beside the algebra

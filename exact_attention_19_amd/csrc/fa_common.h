@@ -159,45 +159,56 @@ __device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 
 // multiple of 4), so the XOR pattern of a lane is the same for every chunk.
 // Rows past `nrows` (the number of valid rows from row0) re-read row
 // nrows - 1 of the tile.
-// Wave-uniform pointer, made explicit so that address arithmetic on it stays
-// in scalar registers.
-__device__ __forceinline__ const unsigned char* uniform_ptr(const unsigned char* p) {
+// Scalar (wave-uniform) copy of a value the compiler cannot prove uniform,
+// e.g. the result of an integer division of uniform operands.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ const unsigned char* uniform(const unsigned char* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
   return reinterpret_cast<const unsigned char*>(((uint64_t)hi << 32) | lo);
 }
 
-template <int NCHUNK>
-__device__ __forceinline__ void dma_tile_d128(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
-                                              unsigned char* lds_tile, int first, int step, int lane) {
+// Buffer resource over the byte range [base, base + bytes): loads at offsets
+// past `bytes` return zero. (Raw buffer, stride 0, 32-bit data format.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-lane byte offset of a tile DMA chunk (constant for every chunk the
+// wave issues): row lane/16 of the chunk, 16-byte unit (lane%16) XOR the
+// row's swizzle. Chunks issued by one wave are c = first + STEP*i with STEP a
+// multiple of 4, so (4c + row) % 16 is the same for all of them.
+__device__ __forceinline__ uint32_t dma_lane_offset(int lane, int first, uint32_t stride_bytes) {
   const int lr = lane >> 4;
-  const uint32_t unit_off = 16u * (uint32_t)((lane & 15) ^ tile_swz(4 * first + lr));
-  if (nrows >= 64) {
-    const uint32_t lane_off = (uint32_t)lr * stride_bytes + unit_off;
+  return (uint32_t)lr * stride_bytes + 16u * (uint32_t)((lane & 15) ^ tile_swz(4 * first + lr));
+}
+
+// DMA rows [0, 64) below `tile_base` (row stride `stride_bytes`) into a
+// swizzled LDS tile; rows at or past `nrows` are read as zero. The calling
+// wave issues chunks c = first + STEP*i (4 rows each, i < NCHUNK, STEP a
+// multiple of 4); first and everything scalar here are wave-uniform.
+template <int NCHUNK, int STEP>
+__device__ __forceinline__ void dma_tile_d128(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
+                                              unsigned char* lds_tile, int first, uint32_t lane_off) {
+  static_assert(STEP % 4 == 0, "chunks of one wave must share the swizzle phase");
 #pragma unroll
-    for (int i = 0; i < NCHUNK; ++i) {
-      const int c = first + i * step;
-      const unsigned char* cb = uniform_ptr(tile_base + (size_t)(4u * c) * stride_bytes);
-      __builtin_amdgcn_global_load_lds(cb + lane_off, (lds_void*)(lds_tile + c * 1024), 16, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NCHUNK; ++i) {
-      const int c = first + i * step;
-      const uint32_t r = (uint32_t)min(4 * c + lr, nrows - 1);
-      const unsigned char* tb = uniform_ptr(tile_base);
-      __builtin_amdgcn_global_load_lds(tb + (r * stride_bytes + unit_off), (lds_void*)(lds_tile + c * 1024), 16, 0, 0);
-    }
+  for (int i = 0; i < NCHUNK; ++i) {
+    const int c = first + STEP * i;
+    const int rows = uniform(min(max(nrows - 4 * c, 0), 4));
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(uniform(tile_base + (size_t)(4 * c) * stride_bytes), (uint32_t)uniform(rows * (int)stride_bytes));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_tile + c * 1024), 16, lane_off, 0, 0, 0);
   }
 }
 
 // DMA 64 consecutive floats src[i0 + lane] (indices clamped to `last`) into
 // LDS dst[lane]: one wave instruction.
 __device__ __forceinline__ void dma_vec64_f32(const float* src, int i0, int last, unsigned char* lds_dst, int lane) {
-  const unsigned char* base = uniform_ptr(reinterpret_cast<const unsigned char*>(src));
   const uint32_t idx = (uint32_t)min(i0 + lane, last);
-  __builtin_amdgcn_global_load_lds(base + 4u * idx, (lds_void*)lds_dst, 4, 0, 0);
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(uniform(reinterpret_cast<const unsigned char*>(src)), (uint32_t)uniform(4 * (last + 1)));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, 4u * idx, 0, 0, 0);
 }
 
 // Transposed read of 4 consecutive rows x 1 column per lane from a swizzled

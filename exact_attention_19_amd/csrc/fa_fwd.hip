@@ -298,9 +298,9 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
   const int bh = bid % BH;
   const int rank = bid / BH;
   const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
+  const int b = uniform(bh / Hq);
+  const int hq = uniform(bh - b * Hq);
+  const int hk = uniform(hq / (Hq / Hkv));
 
   const int64_t q_rs = (int64_t)Hq * D;
   const int64_t kv_rs = (int64_t)Hkv * D;
@@ -347,62 +347,68 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
   float l_run = 0.f;
 
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+  const uint32_t dma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * 64 * kv_rs * 2;
     const int nrows = N - t * 64;
-    dma_tile_d128<CPW>(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, lane);
-    dma_tile_d128<CPW>(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES,
-                       lane);
+    dma_tile_d128<CPW, NWAVES>(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, dma_off);
+    dma_tile_d128<CPW, NWAVES>(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave,
+                               dma_off);
   };
 
-  // One 32-key block (keys k0 .. k0+31 of the tile in LDS at ks/vs, block
-  // index kbk): S^T, softmax update, O^T += V^T P^T. Working on 32 keys at a
-  // time keeps the live score and operand registers small.
-  auto block = [&](const unsigned char* ks, const unsigned char* vs, int k0, int kbk, bool need_mask)
-                   __attribute__((always_inline)) {
-    f32x16 sacc = f32x16{};
+  // A 64-key tile is two 32-key blocks, skewed so that independent work sits
+  // side by side for the scheduler: the S^T MFMAs of block 1 beside the
+  // exponentials of block 0, and the P V MFMAs of block 0 beside the
+  // exponentials of block 1.
+  auto scores = [&](const unsigned char* ks, int kbk) __attribute__((always_inline)) {
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (koff ^ (32 * s)));
-      sacc = mfma32(a, qf[s], sacc);
+      acc = mfma32(a, qf[s], acc);
     }
-    // Element e holds key k0 + 32*kbk + 4*hh + c(e) with c(e) = 8*(e/4) + e%4,
-    // a compile-time constant; it is masked iff c(e) > lim, where lim folds
-    // the causal bound (key <= my_q) and the sequence end (key < N). The
-    // branch is wave-uniform and taken only on diagonal or ragged tiles.
-    if (need_mask) {
-      const int base_key = k0 + kbk * 32 + 4 * hh;
-      int lim = N - 1 - base_key;
-      if (CAUSAL) lim = min(lim, my_q - base_key);
+    return acc;
+  };
+  // Element e holds key k0 + 32*kbk + 4*hh + c(e), c(e) = 8*(e/4) + e%4; it
+  // is masked (-inf) past the causal bound or past N.
+  auto apply_mask = [&](f32x16& sc, int k0, int kbk) __attribute__((always_inline)) {
+    const int base_key = k0 + kbk * 32 + 4 * hh;
+    int lim = N - 1 - base_key;
+    if (CAUSAL) lim = min(lim, my_q - base_key);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sacc[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sacc[e];
-    }
-    float mt = sacc[0];
+    for (int e = 0; e < 16; ++e) sc[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc[e];
+  };
+  // Row maximum of a block in log2 units (max3 tree, then the partner lane).
+  auto rowmax = [&](const f32x16& sc) __attribute__((always_inline)) {
+    float m = fmaxf(sc[0], sc[1]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mt = fmaxf(mt, sacc[e]);
-    mt = fmaxf(mt, swap_halves(mt)) * scale_log2;
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+    for (int e = 2; e < 16; e += 2) m = fmaxf(fmaxf(m, sc[e]), sc[e + 1]);
+    return fmaxf(m, swap_halves(m)) * scale_log2;
+  };
+  // P = exp2(S*c - m) as bf16 MFMA operands; this lane's share of the row sum
+  // is accumulated from the same rounded values with v_dot2_f32_bf16 against
+  // (1, 1), so numerator and denominator see identical probabilities.
+  struct Probs { bf16x8 pb[2]; float sum; };
+  auto probs = [&](const f32x16& sc, float neg_m) __attribute__((always_inline)) {
+    Probs r;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+    for (int e = 0; e < 16; ++e) r.pb[e >> 3][e & 7] = (__bf16)fast_exp2(fmaf(sc[e], scale_log2, neg_m));
+    const bf16x2 ones = as_bf16x2(0x3f803f80u);
+    float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 w = __builtin_bit_cast(u32x4, r.pb[h]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t wi = w[i];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(wi), ones, acc, false);
       }
     }
-    const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-    float psum = 0.f;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = fast_exp2(fmaf(sacc[e], scale_log2, neg_m));
-      psum += p;
-      pb[e >> 3][e & 7] = (__bf16)p;
-    }
-    l_run += psum;
+    r.sum = acc;
+    return r;
+  };
+  auto pv = [&](const unsigned char* vs, int kbk, const Probs& pr) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -411,38 +417,87 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
         const i16x4 lo = tr_read(vs + st * 4096 + (voff[0] ^ (64 * db)));
         const i16x4 hi = tr_read(vs + st * 4096 + (voff[1] ^ (64 * db)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma32(a, pb[tt], oacc[db]);
+        oacc[db] = mfma32(a, pr.pb[tt], oacc[db]);
       }
     }
   };
+  auto rescale_o = [&](float alpha) __attribute__((always_inline)) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+  };
 
-  auto tile = [&](const unsigned char* ks, const unsigned char* vs, int k0, bool need_mask)
+  // Lazy rescale: the exponent reference m_run only moves when some row's
+  // block maximum exceeds it by more than kRescaleSlack, so p <= 2^slack and
+  // most blocks skip the O *= alpha pass; O and l always share one reference.
+  auto tile = [&](const unsigned char* ks, const unsigned char* vs, int k0, auto mask_tag)
                   __attribute__((always_inline)) {
-    block(ks, vs, k0, 0, need_mask);
-    block(ks, vs, k0, 1, need_mask);
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s0 = scores(ks, 0);
+    if constexpr (MASK) apply_mask(s0, k0, 0);
+    const float mt0 = rowmax(s0);
+    if (__builtin_amdgcn_ballot_w64(mt0 > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt0);
+      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+      rescale_o(alpha);
+    }
+    f32x16 s1 = scores(ks, 1);
+    const Probs p0 = probs(s0, (m_run == kNegInf) ? 0.f : -m_run);
+    if constexpr (MASK) apply_mask(s1, k0, 1);
+    const float mt1 = rowmax(s1);
+    const bool resc1 = __builtin_amdgcn_ballot_w64(mt1 > m_run + kRescaleSlack) != 0;
+    const float m1 = resc1 ? fmaxf(m_run, mt1) : m_run;
+    pv(vs, 0, p0);
+    const Probs p1 = probs(s1, (m1 == kNegInf) ? 0.f : -m1);
+    l_run += p0.sum;
+    if (resc1) {
+      const float alpha = (m1 == kNegInf) ? 1.f : fast_exp2(m_run - m1);
+      l_run *= alpha;
+      rescale_o(alpha);
+    }
+    m_run = m1;
+    l_run += p1.sum;
+    pv(vs, 1, p1);
   };
 
   // One pipeline step on LDS stage STG (a compile-time constant, so every
   // LDS offset below is an immediate): prefetch tile t+1 into the other
-  // stage, then consume tile t.
-  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+  // stage, then consume tile t. Tiles [0, n_full) need no masking for any
+  // wave of the workgroup and run the unmasked body; the rest (causal
+  // diagonal, ragged end) run the masked body in a second loop.
+  auto step = [&](int t, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
     if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
     const int k0 = t * 64;
     const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
     if (!skip) {
       const unsigned char* ks = smem + STG * STAGE;
-      const bool need_mask = (CAUSAL && (k0 + 63 > qw0)) || (k0 + 64 > N);
-      tile(ks, ks + TILE, k0, need_mask);
+      tile(ks, ks + TILE, k0, mask_tag);
     }
     __syncthreads();
   };
+  int n_full = N / 64;
+  if (CAUSAL) n_full = min(n_full, q0 / 64);
+  n_full = min(n_full, n_tiles);
 
   issue(0, 0);
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    step(t, std::integral_constant<int, 0>{}, std::false_type{});
+    step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  if (t < n_full) {
+    step(t, std::integral_constant<int, 0>{}, std::false_type{});
+    ++t;
+  }
+  for (; t < n_tiles; ++t) {
+    if ((t & 1) == 0) step(t, std::integral_constant<int, 0>{}, std::true_type{});
+    else step(t, std::integral_constant<int, 1>{}, std::true_type{});
   }
 
   if (!wave_active) return;
