@@ -500,8 +500,18 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int BHK = B * Hkv;
-  const int bhk = blockIdx.x % BHK;
-  const int kt = blockIdx.x / BHK;
+  const int nkt = (N + BKV - 1) / BKV;
+  int bhk, kt;
+  if (BHK % 8 == 0) {
+    // Workgroups are dealt round-robin to the 8 XCDs: keep every key tile of
+    // kv head h on XCD h % 8, so the query tiles they all stream share its L2.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bhk = (slot / nkt) * 8 + xcd;
+    kt = slot % nkt;
+  } else {
+    bhk = blockIdx.x % BHK;
+    kt = blockIdx.x / BHK;  // low key tiles see the most query tiles: launched first
+  }
   const int b = uniform(bhk / Hkv);
   const int hk = uniform(bhk - b * Hkv);
   const int G = Hq / Hkv;
@@ -682,8 +692,17 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   const int l32 = lane & 31, hh = lane >> 5;
 
   const int BH = B * Hq;
-  const int bh = blockIdx.x % BH;
-  const int rank = blockIdx.x / BH;
+  int bh, rank;
+  if (BH % 8 == 0) {
+    // Every query tile of head h on XCD h % 8 (workgroups are dealt
+    // round-robin to the XCDs), so the K/V tiles they stream share its L2.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    bh = (slot / num_q_tiles) * 8 + xcd;
+    rank = slot % num_q_tiles;
+  } else {
+    bh = blockIdx.x % BH;
+    rank = blockIdx.x / BH;
+  }
   const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
   const int b = uniform(bh / Hq);
   const int hq = uniform(bh - b * Hq);

@@ -211,6 +211,23 @@ __device__ __forceinline__ void dma_vec64_f32(const float* src, int i0, int last
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, 4u * idx, 0, 0, 0);
 }
 
+// Wait until at most N vector-memory operations of this wave are in flight
+// (s_waitcnt vmcnt(N); expcnt and lgkmcnt left unconstrained). N <= 63.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): LDS reads
+// are complete (lgkmcnt 0), but vector-memory operations (in-flight tile
+// DMAs) may stay outstanding; callers wait for those with wait_vmcnt first.
+__device__ __forceinline__ void barrier_keep_dma() {
+  __builtin_amdgcn_s_waitcnt((15 & 15) | ((63 >> 4) << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Transposed read of 4 consecutive rows x 1 column per lane from a swizzled
 // d=128 tile: within each group of 16 lanes, lane j addresses row
 // r0 + j/4, columns 16*cg + 4*(j%4) .. +3 (cg picks the 16-column half of a

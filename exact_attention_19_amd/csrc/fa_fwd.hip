@@ -274,8 +274,8 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
 // 4-row blocks are exactly the key groups the score accumulator hands to one
 // 16-key MFMA step: elements 0-3 are keys 16*st + 4*hh + {0..3}, elements
 // 4-7 are keys 16*st + 8 + 4*hh + {0..3}.
-template <int NWAVES, bool CAUSAL>
-__global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
+template <int NWAVES, int NSTAGE, bool CAUSAL>
+__global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
     int num_q_tiles) {
@@ -295,8 +295,17 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
 
   const int BH = B * Hq;
   const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int rank = bid / BH;
+  int bh, rank;
+  if (BH % 8 == 0) {
+    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD whole
+    // heads (every query tile of head h on XCD h % 8) so its L2 holds them.
+    const int xcd = bid & 7, slot = bid >> 3;
+    bh = (slot / num_q_tiles) * 8 + xcd;
+    rank = slot % num_q_tiles;
+  } else {
+    bh = bid % BH;
+    rank = bid / BH;
+  }
   const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
   const int b = uniform(bh / Hq);
   const int hq = uniform(bh - b * Hq);
@@ -464,41 +473,54 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_d128_kernel(
     pv(vs, 1, p1);
   };
 
-  // One pipeline step on LDS stage STG (a compile-time constant, so every
-  // LDS offset below is an immediate): prefetch tile t+1 into the other
-  // stage, then consume tile t. Tiles [0, n_full) need no masking for any
-  // wave of the workgroup and run the unmasked body; the rest (causal
-  // diagonal, ragged end) run the masked body in a second loop.
+  // Tiles are prefetched NSTAGE - 1 ahead into a ring of LDS stages. Step t
+  // (on stage t % NSTAGE, a compile-time constant so LDS offsets are
+  // immediates) issues tile t + NSTAGE - 1 into the stage freed by step
+  // t - 1, consumes tile t, then waits until tile t + 1 has landed (the
+  // DMAs of later tiles may stay in flight) before the workgroup barrier.
+  // Tiles [0, n_full) need no masking for any wave of the workgroup and run
+  // the unmasked body; the rest (causal diagonal, ragged end) run the masked
+  // body in a second loop.
+  static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
+  constexpr int DMA_PER_STEP = 2 * CPW;  // K and V chunks issued by each wave
   auto step = [&](int t, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
+    const bool more = t + NSTAGE - 1 < n_tiles;
+    if (more) issue(t + NSTAGE - 1, (STG + NSTAGE - 1) % NSTAGE);
     const int k0 = t * 64;
     const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
     if (!skip) {
       const unsigned char* ks = smem + STG * STAGE;
       tile(ks, ks + TILE, k0, mask_tag);
     }
-    __syncthreads();
+    if (more) wait_vmcnt<(NSTAGE - 2) * DMA_PER_STEP>();
+    else wait_vmcnt<0>();
+    barrier_keep_dma();
+  };
+  auto step_any = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    const int stg = t % NSTAGE;
+    if (stg == 0) step(t, std::integral_constant<int, 0>{}, mask_tag);
+    else if (NSTAGE > 1 && stg == 1) step(t, std::integral_constant<int, 1 % NSTAGE>{}, mask_tag);
+    else step(t, std::integral_constant<int, 2 % NSTAGE>{}, mask_tag);
   };
   int n_full = N / 64;
   if (CAUSAL) n_full = min(n_full, q0 / 64);
   n_full = min(n_full, n_tiles);
 
-  issue(0, 0);
-  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NSTAGE - 1; ++i) {
+    if (i < n_tiles) issue(i, i);
+  }
+  wait_vmcnt<0>();
+  barrier_keep_dma();
   int t = 0;
-  for (; t + 1 < n_full; t += 2) {
+  for (; t + NSTAGE <= n_full; t += NSTAGE) {
     step(t, std::integral_constant<int, 0>{}, std::false_type{});
-    step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    step(t + 1, std::integral_constant<int, 1 % NSTAGE>{}, std::false_type{});
+    if constexpr (NSTAGE == 3) step(t + 2, std::integral_constant<int, 2>{}, std::false_type{});
   }
-  if (t < n_full) {
-    step(t, std::integral_constant<int, 0>{}, std::false_type{});
-    ++t;
-  }
-  for (; t < n_tiles; ++t) {
-    if ((t & 1) == 0) step(t, std::integral_constant<int, 0>{}, std::true_type{});
-    else step(t, std::integral_constant<int, 1>{}, std::true_type{});
-  }
+  for (; t < n_full; ++t) step_any(t, std::false_type{});
+  for (; t < n_tiles; ++t) step_any(t, std::true_type{});
 
   if (!wave_active) return;
   const float l_tot = l_run + swap_halves(l_run);
@@ -606,14 +628,14 @@ hipError_t launch_bf16(const FwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int NWAVES, bool CAUSAL>
+template <int NWAVES, int NSTAGE, bool CAUSAL>
 hipError_t launch_d128(const FwdArgs& a) {
   constexpr int BM = NWAVES * 32;
   const int num_q_tiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  constexpr size_t smem = 2 * 2 * 64 * 256;
-  auto kern = fwd_d128_kernel<NWAVES, CAUSAL>;
+  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256;
+  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, CAUSAL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
@@ -643,7 +665,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   if (a.d == 64) {
     return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
   }
-  return a.causal ? launch_d128<4, true>(a) : launch_d128<4, false>(a);
+  return a.causal ? launch_d128<4, 2, true>(a) : launch_d128<4, 2, false>(a);
 }
 
 }  // namespace fa
