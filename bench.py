@@ -36,13 +36,14 @@ sys.path.insert(0, ROOT)
 METRIC = "attention TFLOP/s at 1 MI355X (% bf16 MFMA peak); decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 FLOP/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_causal_fwd_bwd_N8192_H96_d128_and_decode_B64_L32k.txt")
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": "fa_fwd.hip",
     "bwd_dkdv_kernel": "fa_bwd.hip",
     "bwd_dq_kernel": "fa_bwd.hip",
     "bwd_preprocess_kernel": "fa_bwd.hip",
     "decode_split_kernel": "fa_decode.hip",
+    "decode_merge_kernel": "fa_decode.hip",
 }
 
 
@@ -54,7 +55,25 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle sample")
     ap.add_argument("--no-decode", action="store_true", help="leave the decode stage out (profiling only)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    """A copy kernel of known size: an elementwise kernel (y = x * 1 in fp32)
+    that reads and writes exactly `mib` MiB per launch."""
+    import torch
+
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": 4 * n, "launches": 3}))
 
 
 def source_sha(name: str) -> str:
@@ -129,6 +148,9 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(pass --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
