@@ -553,9 +553,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     const int q0 = (qt0 + it % per_head) * BQ;
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
-    dma_tile_d128<4, 4>(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, dma_off);
-    dma_tile_d128<4, 4>(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave,
-                        dma_off);
+    dma_rows64(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, 4, 4, dma_off);
+    dma_rows64(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave, 4, 4, dma_off);
     const int64_t vb = ((int64_t)b * Hq + hq) * N;
     if (wave == 0) dma_vec64_f32(lse2 + vb, q0, N - 1, st + VEC_OFF, lane);
     if (wave == 1) dma_vec64_f32(delta + vb, q0, N - 1, st + VEC_OFF + 256, lane);
@@ -748,8 +747,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * BN * kv_rs * 2;
-    dma_tile_d128<4, 4>(kbase + off, kv_rs_bytes, N - t * BN, st, wave, dma_off);
-    dma_tile_d128<4, 4>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, dma_off);
+    dma_rows64(kbase + off, kv_rs_bytes, N - t * BN, st, wave, 4, 4, dma_off);
+    dma_rows64(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, 4, dma_off);
   };
 
   // Same skew as the dK/dV kernel: scores of key block 1 beside the algebra

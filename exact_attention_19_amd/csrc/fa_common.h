@@ -52,8 +52,17 @@ template <typename T>
 __device__ __forceinline__ T max3(T a, T b, T c) { return fmaxf(fmaxf(a, b), c); }
 
 // Value of lane (l ^ 32): exchange between the two halves of the wave.
-__device__ __forceinline__ float swap_halves(float x) {
-  return __shfl_xor(x, 32, 64);
+// Max and sum of x over the lane pair (l, l ^ 32), the same value in both
+// lanes. v_permlane32_swap with x as both operands hands every lane the
+// lower-half value in the first result and the upper-half value in the
+// second, in the VALU (no LDS round trip as with a shuffle).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int CTRL>
@@ -152,13 +161,6 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 __device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
-// DMA rows [row0, row0 + 64) of a [rows][128] bf16 matrix (row stride
-// `stride_bytes`) into a swizzled LDS tile. The calling wave issues chunks
-// c = first + i * step (4 rows each, i < NCHUNK); first and step are
-// wave-uniform and `first % 4 == (first + i * step) % 4` must hold (step a
-// multiple of 4), so the XOR pattern of a lane is the same for every chunk.
-// Rows past `nrows` (the number of valid rows from row0) re-read row
-// nrows - 1 of the tile.
 // Scalar (wave-uniform) copy of a value the compiler cannot prove uniform,
 // e.g. the result of an integer division of uniform operands.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -184,21 +186,28 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int lane, int first, uint32_
   return (uint32_t)lr * stride_bytes + 16u * (uint32_t)((lane & 15) ^ tile_swz(4 * first + lr));
 }
 
-// DMA rows [0, 64) below `tile_base` (row stride `stride_bytes`) into a
-// swizzled LDS tile; rows at or past `nrows` are read as zero. The calling
-// wave issues chunks c = first + STEP*i (4 rows each, i < NCHUNK, STEP a
-// multiple of 4); first and everything scalar here are wave-uniform.
-template <int NCHUNK, int STEP>
-__device__ __forceinline__ void dma_tile_d128(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
-                                              unsigned char* lds_tile, int first, uint32_t lane_off) {
-  static_assert(STEP % 4 == 0, "chunks of one wave must share the swizzle phase");
+// Tile DMA: rows [0, 64) below `tile_base` (row stride `stride_bytes`) go
+// into a swizzled LDS tile; rows at or past `nrows` arrive as zeros. The
+// calling wave issues chunks c = first + step*i (4 rows each, i < nchunk,
+// step a multiple of 4, so every chunk of a lane has the same swizzle phase:
+// lane_off, from dma_lane_offset, is the lane's offset inside its chunk, and
+// chunk c starts 4*c*stride_bytes into the tile). One buffer
+// resource spans the tile's valid rows, so a tile costs a few scalar
+// instructions, one add per chunk and one load per chunk. tile_base and
+// nrows must be wave-uniform; first, step and nchunk are compile-time
+// constants at every call site (the loop unrolls after inlining).
+__device__ __forceinline__ void dma_rows64(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
+                                           unsigned char* lds_tile, int first, int step, int nchunk,
+                                           uint32_t lane_off) {
+  const uint32_t rows = (uint32_t)uniform(min(max(nrows, 0), 64));
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform(tile_base), rows * stride_bytes);
+  const uint32_t chunk_stride = (uint32_t)(4 * step) * stride_bytes;
+  const uint32_t first_off = lane_off + (uint32_t)(4 * first) * stride_bytes;
 #pragma unroll
-  for (int i = 0; i < NCHUNK; ++i) {
-    const int c = first + STEP * i;
-    const int rows = uniform(min(max(nrows - 4 * c, 0), 4));
-    const __amdgpu_buffer_rsrc_t r =
-        make_rsrc(uniform(tile_base + (size_t)(4 * c) * stride_bytes), (uint32_t)uniform(rows * (int)stride_bytes));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_tile + c * 1024), 16, lane_off, 0, 0, 0);
+  for (int i = 0; i < nchunk; ++i) {
+    const int c = first + step * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_tile + c * 1024), 16, first_off + i * chunk_stride,
+                                             0, 0, 0);
   }
 }
 

@@ -31,6 +31,9 @@ constexpr int kBN = 64;  // keys per tile
 // The running maximum used as the exponent reference is only raised when a
 // row's new maximum exceeds it by more than this many powers of two.
 constexpr float kRescaleSlack = 8.f;
+// d = 128 path: a block's probabilities are accepted against a stale
+// reference while each lane's sum of its 16 values stays at or below this.
+constexpr float kSumLimit = 256.f;
 
 template <int D, int NWAVES>
 struct FwdSmem {
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
           mt = fmaxf(mt, x);
         }
       }
-      mt = fmaxf(mt, swap_halves(mt)) * scale_log2;  // log2 units (scale > 0)
+      mt = pair_max(mt) * scale_log2;  // log2 units (scale > 0)
       // Lazy rescale: the reference maximum m_run only moves when some row's
       // maximum exceeds it by more than kRescaleSlack, so p <= 2^kRescaleSlack.
       // O and l always share the same reference, so the result is unchanged;
@@ -247,7 +250,7 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
   }
 
   if (!wave_active) return;
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = pair_sum(l_run);
   if (my_q < N) {
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
@@ -274,13 +277,19 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
 // 4-row blocks are exactly the key groups the score accumulator hands to one
 // 16-key MFMA step: elements 0-3 are keys 16*st + 4*hh + {0..3}, elements
 // 4-7 are keys 16*st + 8 + 4*hh + {0..3}.
-template <int NWAVES, int NSTAGE, bool CAUSAL>
-__global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
+//
+// Each wave owns QB blocks of 32 query rows. Every K operand and V^T operand
+// read from LDS feeds QB MFMAs (one per query block), so LDS read traffic per
+// MFMA falls as 1/QB; with QB = 2 the O accumulators (128 registers) and the
+// Q operands (64) need one wave per SIMD.
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL>
+__global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
     int num_q_tiles) {
   constexpr int D = 128;
-  constexpr int BM = NWAVES * 32;
+  constexpr int WQ = 32 * QB;           // query rows per wave
+  constexpr int BM = NWAVES * WQ;       // query rows per workgroup
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
   constexpr int TILE = 64 * 256;        // bytes of one 64 x 128 bf16 tile
@@ -317,15 +326,18 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
   const __bf16* vb = v + ((int64_t)b * N) * kv_rs + (int64_t)hk * D;
 
   const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
+  const int qw0 = q0 + wave * WQ;
   const bool wave_active = qw0 < N;
-
-  bf16x8 qf[DS];
-  {
-    const __bf16* qrow = q + ((int64_t)b * N + min(my_q, N - 1)) * q_rs + (int64_t)hq * D + 8 * hh;
+  int my_q[QB];
 #pragma unroll
-    for (int s = 0; s < DS; ++s) qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
+  for (int j = 0; j < QB; ++j) my_q[j] = qw0 + 32 * j + l32;
+
+  bf16x8 qf[QB][DS];
+#pragma unroll
+  for (int j = 0; j < QB; ++j) {
+    const __bf16* qrow = q + ((int64_t)b * N + min(my_q[j], N - 1)) * q_rs + (int64_t)hq * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qf[j][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
   }
 
   int kv_end = N;
@@ -349,11 +361,15 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
     }
   }
 
-  f32x16 oacc[DB];
+  f32x16 oacc[QB][DB];
+  float m_run[QB], l_run[QB];
 #pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = kNegInf;
-  float l_run = 0.f;
+  for (int j = 0; j < QB; ++j) {
+#pragma unroll
+    for (int i = 0; i < DB; ++i) oacc[j][i] = f32x16{};
+    m_run[j] = kNegInf;
+    l_run[j] = 0.f;
+  }
 
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
   const uint32_t dma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
@@ -361,39 +377,46 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * 64 * kv_rs * 2;
     const int nrows = N - t * 64;
-    dma_tile_d128<CPW, NWAVES>(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, dma_off);
-    dma_tile_d128<CPW, NWAVES>(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave,
-                               dma_off);
+    dma_rows64(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, CPW, dma_off);
+    dma_rows64(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES, CPW,
+               dma_off);
   };
 
   // A 64-key tile is two 32-key blocks, skewed so that independent work sits
   // side by side for the scheduler: the S^T MFMAs of block 1 beside the
   // exponentials of block 0, and the P V MFMAs of block 0 beside the
   // exponentials of block 1.
+  struct Sc { f32x16 s[QB]; };
   auto scores = [&](const unsigned char* ks, int kbk) __attribute__((always_inline)) {
-    f32x16 acc = f32x16{};
+    Sc r;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) r.s[j] = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (koff ^ (32 * s)));
-      acc = mfma32(a, qf[s], acc);
-    }
-    return acc;
-  };
-  // Element e holds key k0 + 32*kbk + 4*hh + c(e), c(e) = 8*(e/4) + e%4; it
-  // is masked (-inf) past the causal bound or past N.
-  auto apply_mask = [&](f32x16& sc, int k0, int kbk) __attribute__((always_inline)) {
-    const int base_key = k0 + kbk * 32 + 4 * hh;
-    int lim = N - 1 - base_key;
-    if (CAUSAL) lim = min(lim, my_q - base_key);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc[e];
+      for (int j = 0; j < QB; ++j) r.s[j] = mfma32(a, qf[j][s], r.s[j]);
+    }
+    return r;
+  };
+  // Element e of query block j holds key k0 + 32*kbk + 4*hh + c(e),
+  // c(e) = 8*(e/4) + e%4; it is masked (-inf) past the causal bound or past N.
+  auto apply_mask = [&](Sc& sc, int k0, int kbk) __attribute__((always_inline)) {
+    const int base_key = k0 + kbk * 32 + 4 * hh;
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      int lim = N - 1 - base_key;
+      if (CAUSAL) lim = min(lim, my_q[j] - base_key);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc.s[j][e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc.s[j][e];
+    }
   };
   // Row maximum of a block in log2 units (max3 tree, then the partner lane).
   auto rowmax = [&](const f32x16& sc) __attribute__((always_inline)) {
     float m = fmaxf(sc[0], sc[1]);
 #pragma unroll
     for (int e = 2; e < 16; e += 2) m = fmaxf(fmaxf(m, sc[e]), sc[e + 1]);
-    return fmaxf(m, swap_halves(m)) * scale_log2;
+    return pair_max(m) * scale_log2;
   };
   // P = exp2(S*c - m) as bf16 MFMA operands; this lane's share of the row sum
   // is accumulated from the same rounded values with v_dot2_f32_bf16 against
@@ -417,7 +440,7 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
     r.sum = acc;
     return r;
   };
-  auto pv = [&](const unsigned char* vs, int kbk, const Probs& pr) __attribute__((always_inline)) {
+  auto pv = [&](const unsigned char* vs, int kbk, const Probs* pr) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -426,50 +449,77 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
         const i16x4 lo = tr_read(vs + st * 4096 + (voff[0] ^ (64 * db)));
         const i16x4 hi = tr_read(vs + st * 4096 + (voff[1] ^ (64 * db)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        oacc[db] = mfma32(a, pr.pb[tt], oacc[db]);
+#pragma unroll
+        for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32(a, pr[j].pb[tt], oacc[j][db]);
       }
     }
   };
-  auto rescale_o = [&](float alpha) __attribute__((always_inline)) {
+  // O *= alpha for query block j. With one query block the accumulators sit
+  // in VGPRs and are scaled in place. With two they live in AGPRs, where the
+  // MFMAs read and write them; scaling them in place would make the register
+  // allocator keep them in VGPRs instead (and spill), so the rare rescale goes
+  // through a 4 KB per-wave LDS slot: store, scale in VGPRs, store, load
+  // back, with compiler barriers so the round trip stays.
+  float* resc_slot = reinterpret_cast<float*>(smem + NSTAGE * STAGE + wave * 4096) + lane * 16;
+  auto rescale_o = [&](int j, float alpha) __attribute__((always_inline)) {
+    if constexpr (QB == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[j][db][e] *= alpha;
+      }
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
+      *reinterpret_cast<f32x16*>(resc_slot) = oacc[j][db];
+      asm volatile("" ::: "memory");
+      f32x16 t = *reinterpret_cast<const f32x16*>(resc_slot);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+      for (int e = 0; e < 16; ++e) t[e] *= alpha;
+      *reinterpret_cast<f32x16*>(resc_slot) = t;
+      asm volatile("" ::: "memory");
+      oacc[j][db] = *reinterpret_cast<const f32x16*>(resc_slot);
     }
   };
 
-  // Lazy rescale: the exponent reference m_run only moves when some row's
-  // block maximum exceeds it by more than kRescaleSlack, so p <= 2^slack and
-  // most blocks skip the O *= alpha pass; O and l always share one reference.
+  // Lazy rescale. P is first formed against the current reference m_run
+  // (no row maximum in the common path). Each lane sums its 16 new
+  // probabilities anyway; if no lane's sum exceeds kSumLimit, every p is at
+  // most kSumLimit and the block is accepted as is. Otherwise (the reference
+  // is stale by more than log2(kSumLimit), or it is still -inf, which makes
+  // the sum inf or NaN) the rare path takes the block's row maximum, moves
+  // the reference there, rescales O and l, and recomputes P. O and l always
+  // share one reference.
+  auto resync = [&](int j, const f32x16& sc) __attribute__((always_inline)) {
+    const float m_new = fmaxf(m_run[j], rowmax(sc));
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run[j] - m_new);
+    l_run[j] *= alpha;
+    rescale_o(j, alpha);
+    m_run[j] = m_new;
+    return probs(sc, (m_new == kNegInf) ? 0.f : -m_new);
+  };
   auto tile = [&](const unsigned char* ks, const unsigned char* vs, int k0, auto mask_tag)
                   __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 s0 = scores(ks, 0);
+    Sc s0 = scores(ks, 0);
     if constexpr (MASK) apply_mask(s0, k0, 0);
-    const float mt0 = rowmax(s0);
-    if (__builtin_amdgcn_ballot_w64(mt0 > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt0);
-      const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-      rescale_o(alpha);
-    }
-    f32x16 s1 = scores(ks, 1);
-    const Probs p0 = probs(s0, (m_run == kNegInf) ? 0.f : -m_run);
+    Sc s1 = scores(ks, 1);
     if constexpr (MASK) apply_mask(s1, k0, 1);
-    const float mt1 = rowmax(s1);
-    const bool resc1 = __builtin_amdgcn_ballot_w64(mt1 > m_run + kRescaleSlack) != 0;
-    const float m1 = resc1 ? fmaxf(m_run, mt1) : m_run;
-    pv(vs, 0, p0);
-    const Probs p1 = probs(s1, (m1 == kNegInf) ? 0.f : -m1);
-    l_run += p0.sum;
-    if (resc1) {
-      const float alpha = (m1 == kNegInf) ? 1.f : fast_exp2(m_run - m1);
-      l_run *= alpha;
-      rescale_o(alpha);
+    Probs p0[QB], p1[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      p0[j] = probs(s0.s[j], -m_run[j]);
+      if (__builtin_amdgcn_ballot_w64(!(p0[j].sum <= kSumLimit))) p0[j] = resync(j, s0.s[j]);
+      l_run[j] += p0[j].sum;
     }
-    m_run = m1;
-    l_run += p1.sum;
+    pv(vs, 0, p0);
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      p1[j] = probs(s1.s[j], -m_run[j]);
+      if (__builtin_amdgcn_ballot_w64(!(p1[j].sum <= kSumLimit))) p1[j] = resync(j, s1.s[j]);
+      l_run[j] += p1[j].sum;
+    }
     pv(vs, 1, p1);
   };
 
@@ -488,7 +538,7 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
     const bool more = t + NSTAGE - 1 < n_tiles;
     if (more) issue(t + NSTAGE - 1, (STG + NSTAGE - 1) % NSTAGE);
     const int k0 = t * 64;
-    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + WQ - 1);
     if (!skip) {
       const unsigned char* ks = smem + STG * STAGE;
       tile(ks, ks + TILE, k0, mask_tag);
@@ -523,22 +573,25 @@ __global__ __launch_bounds__(NWAVES * 64, 8 / NWAVES) void fwd_d128_kernel(
   for (; t < n_tiles; ++t) step_any(t, std::true_type{});
 
   if (!wave_active) return;
-  const float l_tot = l_run + swap_halves(l_run);
-  if (my_q < N) {
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    __bf16* orow = o + ((int64_t)b * N + my_q) * q_rs + (int64_t)hq * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int j = 0; j < QB; ++j) {
+    const float l_tot = pair_sum(l_run[j]);
+    if (my_q[j] < N) {
+      const bool empty = !(l_tot > 0.f);
+      const float inv = empty ? 0.f : 1.f / l_tot;
+      __bf16* orow = o + ((int64_t)b * N + my_q[j]) * q_rs + (int64_t)hq * D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hh) = w;
+      for (int db = 0; db < DB; ++db) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          u32x2 w;
+          w[0] = pack_bf16x2(oacc[j][db][4 * i + 0] * inv, oacc[j][db][4 * i + 1] * inv);
+          w[1] = pack_bf16x2(oacc[j][db][4 * i + 2] * inv, oacc[j][db][4 * i + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * i + 4 * hh) = w;
+        }
       }
+      if (hh == 0) lse[((int64_t)b * Hq + hq) * N + my_q[j]] = empty ? kNegInf : (m_run[j] + __log2f(l_tot)) * kLn2;
     }
-    if (hh == 0) lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -628,14 +681,14 @@ hipError_t launch_bf16(const FwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int NWAVES, int NSTAGE, bool CAUSAL>
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL>
 hipError_t launch_d128(const FwdArgs& a) {
-  constexpr int BM = NWAVES * 32;
+  constexpr int BM = NWAVES * 32 * QB;
   const int num_q_tiles = (a.N + BM - 1) / BM;
   const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256;
-  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, CAUSAL>;
+  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + NWAVES * 4096;  // tile ring + rescale slots
+  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
@@ -665,7 +718,7 @@ hipError_t launch_fwd(const FwdArgs& a) {
   if (a.d == 64) {
     return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
   }
-  return a.causal ? launch_d128<4, 2, true>(a) : launch_d128<4, 2, false>(a);
+  return a.causal ? launch_d128<4, 2, 1, true>(a) : launch_d128<4, 2, 1, false>(a);
 }
 
 }  // namespace fa

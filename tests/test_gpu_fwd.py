@@ -57,6 +57,7 @@ SWEEP = [
     (1, 200, 8, 8, 128),
     (1, 1000, 4, 1, 128),
     (1, 333, 16, 2, 64),
+    (1, 2113, 2, 1, 128),
 ]
 
 
@@ -143,3 +144,27 @@ def test_error_no_larger_than_twice_bf16_baseline():
     gpu_err, _ = errors(o, ro)
     base_err, _ = errors(base, ro)
     assert gpu_err <= 2 * base_err + 1e-6, (gpu_err, base_err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores_rescale_running_output(d, causal):
+    """Key norms grow along the sequence (x0.1 at the start to x12 at the end),
+    so a row's running maximum rises by far more than the kernel's rescale
+    slack several times after O has accumulated real contributions: every
+    rescale of a non-zero O is exercised and checked against the oracle."""
+    fa = need_gpu()
+    B, N, Hq, Hkv = 1, 1500, 4, 2
+    announce(f"fwd rising scores N{N} d{d} causal={causal}")
+    inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=5)
+    gain = torch.linspace(0.1, 12.0, N, dtype=torch.float32).view(1, N, 1, 1)
+    inp["k"] = (inp["k"].float() * gain).to(torch.bfloat16)
+    o, lse = _run(fa, inp, causal)
+    ro, rl = oracle.attn_fwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), 1.0 / math.sqrt(d), causal)
+    # the scores really do move: for the last row, the largest score among
+    # the last 256 keys exceeds that among the first 256 by > 20 (natural log)
+    qn, kn = f64(inp["q"])[0, N - 1, 0], f64(inp["k"])[0, :, 0]
+    sc = kn @ qn / math.sqrt(d)
+    assert sc[N - 256:].max() - sc[:256].max() > 20.0
+    assert_bf16_close(o, ro, "O")
+    assert_bf16_close(lse, rl, "LSE")
