@@ -28,6 +28,14 @@
 
 namespace fa {
 
+// VALU instructions placed after each MFMA in the pinned dQ schedule.
+#ifndef DQ_SGB_VALU0
+#define DQ_SGB_VALU0 3
+#endif
+#ifndef DQ_SGB_VALU1
+#define DQ_SGB_VALU1 6
+#endif
+
 namespace {
 
 constexpr int kBwdThreads = 256;
@@ -533,10 +541,33 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     }
   }
 
+  // Query tiles of each head in the group, in two phases: first every tile
+  // that needs masking for some wave of the workgroup (the causal diagonal,
+  // q0 < k0 + BKV - 1, and a ragged last tile), for all heads; then all
+  // full tiles. Each phase is a loop with its own body, so the full tiles
+  // run a branch-free body.
   const int nqt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-  const int per_head = nqt - qt0;
-  const int n_iter = G * per_head;
+  const int m_hi = CAUSAL ? min(nqt, qt0 + (BKV + BQ - 2) / BQ + 1) : qt0;  // diagonal tiles [qt0, m_hi)
+  const bool ragged_extra = (N % BQ != 0) && (nqt - 1 >= m_hi);
+  const int n_m = (m_hi - qt0) + (ragged_extra ? 1 : 0);                    // masked tiles per head
+  const int u_hi = nqt - (ragged_extra ? 1 : 0);
+  const int n_u = u_hi - m_hi;                                               // full tiles per head
+  const int n1 = G * n_m;
+  const int n_iter = n1 + G * n_u;
+  // Iteration it -> (query head, first query row).
+  auto tile_of = [&](int it, int& hq, int& q0) __attribute__((always_inline)) {
+    if (it < n1) {
+      const int h = uniform(it / n_m), j = it - h * n_m;
+      hq = hk * G + h;
+      q0 = (j < m_hi - qt0 ? qt0 + j : nqt - 1) * BQ;
+    } else {
+      const int i2 = it - n1;
+      const int h = uniform(i2 / n_u), j = i2 - h * n_u;
+      hq = hk * G + h;
+      q0 = (m_hi + j) * BQ;
+    }
+  };
 
   const int roff = row_offset(lane);
   int toff[2];
@@ -549,8 +580,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
 
   auto issue = [&](int it, int stage) __attribute__((always_inline)) {
-    const int hq = hk * G + it / per_head;
-    const int q0 = (qt0 + it % per_head) * BQ;
+    int hq, q0;
+    tile_of(it, hq, q0);
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
     dma_rows64(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, 4, 4, dma_off);
@@ -625,36 +656,49 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
       }
     }
   };
-  auto tile_body = [&](const unsigned char* st, int q0, bool need_mask) __attribute__((always_inline)) {
+  // MASK is a compile-time tag: tiles without masking (all but the causal
+  // diagonal and the ragged end) run a branch-free body, one scheduling
+  // region. (Pinning its issue order as in the dQ kernel measured slower
+  // here, with one wave per SIMD; the compiler's order is kept.)
+  auto tile_body = [&](const unsigned char* st, int q0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     Scores s0 = scores(st, 0);
-    if (need_mask) apply_mask(s0, q0, 0);
+    if constexpr (MASK) apply_mask(s0, q0, 0);
     Scores s1 = scores(st, 1);
     const Probs p0 = algebra(st, 0, s0);
-    if (need_mask) apply_mask(s1, q0, 1);
+    if constexpr (MASK) apply_mask(s1, q0, 1);
     update(st, 0, p0);
     const Probs p1 = algebra(st, 1, s1);
     update(st, 1, p1);
   };
 
-  auto step = [&](int it, auto stage_tag) __attribute__((always_inline)) {
+  auto step = [&](int it, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
     if (it + 1 < n_iter) issue(it + 1, STG ^ 1);
-    const int q0 = (qt0 + it % per_head) * BQ;
+    int hq_unused, q0;
+    tile_of(it, hq_unused, q0);
     const bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
-    if (!skip) {
-      const unsigned char* st = smem + STG * STAGE;
-      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (q0 + BQ > N);
-      tile_body(st, q0, need_mask);
-    }
-    __syncthreads();
+    if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag);
+    wait_vmcnt<0>();
+    barrier_keep_dma();
   };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
 
   if (n_iter > 0) issue(0, 0);
-  __syncthreads();
-  for (int it = 0; it < n_iter; it += 2) {
-    step(it, std::integral_constant<int, 0>{});
-    if (it + 1 < n_iter) step(it + 1, std::integral_constant<int, 1>{});
+  wait_vmcnt<0>();
+  barrier_keep_dma();
+  int it = 0;
+  for (; it < n1; ++it) {
+    if ((it & 1) == 0) step(it, S0{}, std::true_type{});
+    else step(it, S1{}, std::true_type{});
   }
+  if (it < n_iter && (it & 1)) step(it++, S1{}, std::false_type{});
+  for (; it + 1 < n_iter; it += 2) {
+    step(it, S0{}, std::false_type{});
+    step(it + 1, S1{}, std::false_type{});
+  }
+  if (it < n_iter) step(it, S0{}, std::false_type{});
 
   if (!wave_active || my_key >= N) return;
   const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
@@ -793,35 +837,70 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
       }
     }
   };
-  auto tile_body = [&](const unsigned char* st, int k0, bool need_mask) __attribute__((always_inline)) {
+  // MASK is a compile-time tag: tiles that need no masking (all but the
+  // causal diagonal and the ragged end) run a body without branches, so the
+  // whole tile is one scheduling region and its issue order can be pinned:
+  // the scores of block 0 (with block 1's operand reads in between), the
+  // scores of block 1 interleaved with block 0's algebra, the dQ product of
+  // block 0 interleaved with block 1's algebra, then the dQ product of block 1.
+  auto tile_body = [&](const unsigned char* st, int k0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     Scores s0 = scores(st, 0);
-    if (need_mask) apply_mask(s0, k0, 0);
+    if constexpr (MASK) apply_mask(s0, k0, 0);
     Scores s1 = scores(st, 1);
     const DsB d0 = algebra(s0);
-    if (need_mask) apply_mask(s1, k0, 1);
+    if constexpr (MASK) apply_mask(s1, k0, 1);
     update(st, 0, d0);
     const DsB d1 = algebra(s1);
     update(st, 1, d1);
+    if constexpr (!MASK) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, DQ_SGB_VALU0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, DQ_SGB_VALU1, 0);
+      }
+    }
   };
 
-  auto step = [&](int t, auto stage_tag) __attribute__((always_inline)) {
+  // Two LDS stages: step t issues tile t + 1 into the other stage, consumes
+  // tile t, waits for its own DMAs and meets the other waves at the barrier.
+  auto step = [&](int t, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
     if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
     const int k0 = t * BN;
     const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
-    if (!skip) {
-      const unsigned char* st = smem + STG * STAGE;
-      const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw0)) || (k0 + BN > N);
-      tile_body(st, k0, need_mask);
-    }
-    __syncthreads();
+    if (!skip) tile_body(smem + STG * STAGE, k0, mask_tag);
+    wait_vmcnt<0>();
+    barrier_keep_dma();
   };
+  int n_full = N / BN;
+  if (CAUSAL) n_full = min(n_full, q0 / BN);
+  n_full = min(n_full, n_tiles);
 
   issue(0, 0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < n_tiles) step(t + 1, std::integral_constant<int, 1>{});
+  wait_vmcnt<0>();
+  barrier_keep_dma();
+  int t = 0;
+  for (; t + 1 < n_full; t += 2) {
+    step(t, std::integral_constant<int, 0>{}, std::false_type{});
+    step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+  }
+  for (; t < n_tiles; ++t) {
+    if ((t & 1) == 0) step(t, std::integral_constant<int, 0>{}, std::true_type{});
+    else step(t, std::integral_constant<int, 1>{}, std::true_type{});
   }
 
   if (!wave_active || my_q >= N) return;

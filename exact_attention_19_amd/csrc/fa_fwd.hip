@@ -34,6 +34,10 @@ constexpr float kRescaleSlack = 8.f;
 // d = 128 path: a block's probabilities are accepted against a stale
 // reference while each lane's sum of its 16 values stays at or below this.
 constexpr float kSumLimit = 256.f;
+// VALU instructions placed after each MFMA in the interleaved stretches.
+#ifndef SGB_VALU
+#define SGB_VALU 6
+#endif
 
 template <int D, int NWAVES>
 struct FwdSmem {
@@ -508,15 +512,44 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     if constexpr (MASK) apply_mask(s1, k0, 1);
     Probs p0[QB], p1[QB];
 #pragma unroll
+    for (int j = 0; j < QB; ++j) p0[j] = probs(s0.s[j], -m_run[j]);
+    if constexpr (QB == 1) {
+      // Issue order for this stretch: the 8 K operand reads of block 0, its
+      // 8 MFMAs each followed by one K read of block 1, then the 8 MFMAs of
+      // block 1 each followed by a share of block 0's softmax VALU work.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, SGB_VALU, 0);
+      }
+    }
+#pragma unroll
     for (int j = 0; j < QB; ++j) {
-      p0[j] = probs(s0.s[j], -m_run[j]);
       if (__builtin_amdgcn_ballot_w64(!(p0[j].sum <= kSumLimit))) p0[j] = resync(j, s0.s[j]);
       l_run[j] += p0[j].sum;
     }
     pv(vs, 0, p0);
 #pragma unroll
+    for (int j = 0; j < QB; ++j) p1[j] = probs(s1.s[j], -m_run[j]);
+    if constexpr (QB == 1) {
+      // The P V MFMAs of block 0, each with its two V^T reads and a share of
+      // block 1's softmax VALU work.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, SGB_VALU, 0);
+      }
+    }
+#pragma unroll
     for (int j = 0; j < QB; ++j) {
-      p1[j] = probs(s1.s[j], -m_run[j]);
       if (__builtin_amdgcn_ballot_w64(!(p1[j].sum <= kSumLimit))) p1[j] = resync(j, s1.s[j]);
       l_run[j] += p1[j].sum;
     }
