@@ -37,8 +37,23 @@ What is computed, and where the pages define it:
   query row per (sequence, head) attends keys 0 .. L_b - 1 of its cache
   (with one query the bottom-right causal mask keeps every cached key).
 
-A fully masked row (only possible when causal and Nq > Nk) has O = 0 and
-LSE = -inf by convention.
+* Sliding window (hysenlabs digest: ``window_size`` among the arguments in
+  "出力と運用記録", sliding-window attention in the v2.3 entry of
+  "制約を切り分ける確認"). The pages give no formula; the reading taken is a
+  band about the bottom-right-aligned diagonal: with window (wl, wr), query i
+  keeps key j iff ``i + off - wl <= j <= i + off + wr`` where
+  ``off = Nk - Nq``, and a negative side is unbounded. Causal masking is
+  applied on top (it equals wr = 0).
+* Variable-length batches (the v2.0 entry of the same changelog: the
+  "unpadded" functions became "varlen"): sequences are packed along the row
+  axis and delimited by prefix sums ``cu_q`` / ``cu_k`` (``[B + 1]``,
+  ``cu[0] = 0``); sequence b is an independent attention problem on rows
+  ``cu_q[b]:cu_q[b+1]`` of Q and ``cu_k[b]:cu_k[b+1]`` of K and V, with the
+  bottom-right causal alignment inside each sequence. This packing is a
+  stated reading (the pages only name the functions).
+
+A fully masked row (possible when causal and Nq > Nk, or with a window that
+leaves a row no keys) has O = 0 and LSE = -inf by convention.
 
 Inputs are numpy arrays of any float dtype; they are converted exactly to
 float64. Layouts: q, o, do, dq ``[B, Nq, Hq, d]``; k, v, dk, dv
@@ -55,12 +70,13 @@ def _check_heads(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
-def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=None, nq=None):
+def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=None, nq=None, window=(-1, -1)):
     """Scores, probabilities and logsumexp for one (batch, head).
 
     q: [R, d] query rows, k: [Nk, d] (float64). ``rows`` gives the absolute
     index of each query row among ``nq`` queries (default: all rows,
-    0 .. R-1 of R), which the causal mask needs. Returns (S, P, lse) where S
+    0 .. R-1 of R), which the causal mask and the window need. ``window`` is
+    (wl, wr), a negative side being unbounded. Returns (S, P, lse) where S
     holds -inf at masked positions, P = softmax(S) row-wise (0 where
     masked) and lse = log sum_j exp(S_ij) (-inf for a fully masked row).
     """
@@ -69,9 +85,16 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=No
         rows = np.arange(q.shape[0])
         nq = q.shape[0]
     s = scale * (q @ k.T)
+    diag = np.asarray(rows)[:, None] + (nk - nq)   # the bottom-right-aligned diagonal of each row
+    j = np.arange(nk)[None, :]
     if causal:
-        keep = np.arange(nk)[None, :] <= np.asarray(rows)[:, None] + (nk - nq)
+        keep = j <= diag
         s = np.where(keep, s, -np.inf)
+    wl, wr = window
+    if wl >= 0:
+        s = np.where(j >= diag - wl, s, -np.inf)
+    if wr >= 0:
+        s = np.where(j <= diag + wr, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
@@ -83,8 +106,9 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=No
     return s, p, lse
 
 
-def attn_fwd(q, k, v, scale: float, causal: bool):
-    """O = softmax(Q K^T * scale [+ causal mask]) V and the per-row logsumexp.
+def attn_fwd(q, k, v, scale: float, causal: bool, window=(-1, -1)):
+    """O = softmax(Q K^T * scale [+ causal mask] [+ window]) V and the per-row
+    logsumexp.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]. Returns (o [B, Nq, Hq, d],
     lse [B, Hq, Nq]) in float64.
@@ -100,13 +124,13 @@ def attn_fwd(q, k, v, scale: float, causal: bool):
     for b in range(b_):
         for h in range(hq):
             kh = h // g
-            _, p, lse_bh = head_probs(q[b, :, h, :], k[b, :, kh, :], scale, causal)
+            _, p, lse_bh = head_probs(q[b, :, h, :], k[b, :, kh, :], scale, causal, window=window)
             o[b, :, h, :] = p @ v[b, :, kh, :]
             lse[b, h, :] = lse_bh
     return o, lse
 
 
-def attn_bwd(q, k, v, do, scale: float, causal: bool):
+def attn_bwd(q, k, v, do, scale: float, causal: bool, window=(-1, -1)):
     """Gradients of L = sum(O * dO) with respect to Q, K and V.
 
     P is recomputed from Q and K (nothing from a forward pass is reused).
@@ -128,7 +152,7 @@ def attn_bwd(q, k, v, do, scale: float, causal: bool):
         for h in range(hq):
             kh = h // g
             qh, kk, vv, doh = q[b, :, h, :], k[b, :, kh, :], v[b, :, kh, :], do[b, :, h, :]
-            _, p, _ = head_probs(qh, kk, scale, causal)
+            _, p, _ = head_probs(qh, kk, scale, causal, window=window)
             dv[b, :, kh, :] += p.T @ doh
             dp = doh @ vv.T
             drow = (p * dp).sum(axis=1, keepdims=True)
@@ -163,6 +187,40 @@ def attn_decode(q, k_cache, v_cache, cache_seqlens, scale: float):
             _, p, lse_h = head_probs(q[b, h][None, :], kb[:, kh, :], scale, causal=False)
             o[b, h] = (p @ vb[:, kh, :])[0]
             lse[b, h] = lse_h[0]
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, window=(-1, -1)):
+    """Forward over packed variable-length sequences.
+
+    q: [total_q, Hq, d]; k, v: [total_k, Hkv, d]; cu_q, cu_k: [B + 1]
+    prefix sums of the query and key lengths. Sequence b is the forward of
+    ``attn_fwd`` on rows cu_q[b]:cu_q[b+1] and cu_k[b]:cu_k[b+1].
+    Returns (o [total_q, Hq, d], lse [Hq, total_q]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    if cu_q.shape != cu_k.shape or cu_q[0] != 0 or cu_k[0] != 0:
+        raise ValueError("cu_q and cu_k must be [B + 1] prefix sums starting at 0")
+    if np.any(np.diff(cu_q) < 0) or np.any(np.diff(cu_k) < 0):
+        raise ValueError("sequence lengths must be non-negative")
+    if cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0]:
+        raise ValueError("cu_q[-1] / cu_k[-1] must equal the packed row counts")
+    hq = q.shape[1]
+    o = np.zeros_like(q)
+    lse = np.full((hq, q.shape[0]), -np.inf)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if q1 == q0:
+            continue
+        if k1 == k0:            # no keys: every row is empty (O = 0, LSE = -inf)
+            continue
+        ob, lb = attn_fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], scale, causal, window)
+        o[q0:q1] = ob[0]
+        lse[:, q0:q1] = lb[0]
     return o, lse
 
 

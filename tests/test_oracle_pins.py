@@ -33,6 +33,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
 def _expr(s: str) -> float:
     """Evaluate a golden-file expression: a rational, ln(x), or a*ln(x)."""
     s = s.strip()
+    if s in ("-inf", "inf"):
+        return float(s)
     if "*ln(" in s:
         a, b = s.split("*ln(")
         return float(Fraction(a)) * math.log(float(Fraction(b[:-1])))
@@ -51,7 +53,7 @@ def _rand(rng, *shape):
     return rng.standard_normal(shape)
 
 
-def _brute_fwd(q, k, v, scale, causal):
+def _brute_fwd(q, k, v, scale, causal, window=(-1, -1)):
     """Scalar-loop attention straight from the definition (tiny sizes only)."""
     B, nq, hq, d = q.shape
     nk, hkv = k.shape[1], k.shape[2]
@@ -66,10 +68,17 @@ def _brute_fwd(q, k, v, scale, causal):
                 for j in range(nk):
                     if causal and j > i + (nk - nq):
                         continue
+                    if window[0] >= 0 and j < i + (nk - nq) - window[0]:
+                        continue
+                    if window[1] >= 0 and j > i + (nk - nq) + window[1]:
+                        continue
                     dot = 0.0
                     for c in range(d):
                         dot += q[b, i, h, c] * k[b, j, kh, c]
                     scores.append((j, scale * dot))
+                if not scores:
+                    lse[b, h, i] = -math.inf
+                    continue
                 total = sum(math.exp(sv) for _, sv in scores)
                 lse[b, h, i] = math.log(total)
                 for j, sv in scores:
@@ -320,6 +329,91 @@ PINS = [pin_golden_fwd, pin_golden_bwd, pin_golden_decode, pin_brute_force, pin_
         pin_fwd_rows]
 
 
+def pin_golden_window(m):
+    data = json.load(open(GOLDEN))
+    for case in data["window"]:
+        q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
+        o, lse = m.attn_fwd(q, k, v, _expr(case["scale"]), case["causal"], tuple(case["window"]))
+        np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13, err_msg=case["name"])
+        np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=1e-13, err_msg=case["name"])
+
+
+def pin_golden_varlen(m):
+    data = json.load(open(GOLDEN))
+    for case in data["varlen"]:
+        q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
+        o, lse = m.attn_fwd_varlen(q, k, v, case["cu_q"], case["cu_k"], _expr(case["scale"]), case["causal"])
+        np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13, err_msg=case["name"])
+        np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(_arr(case["lse"])))
+        fin = np.isfinite(_arr(case["lse"]))
+        np.testing.assert_allclose(lse[fin], _arr(case["lse"])[fin], rtol=0, atol=1e-13, err_msg=case["name"])
+
+
+WINDOW_CASES = [(-1, -1), (0, 0), (1, 0), (0, 2), (3, 1), (2, -1), (-1, 2), (20, 20)]
+
+
+def pin_window_brute_force(m):
+    rng = np.random.default_rng(21)
+    for (B, nq, nk, hq, hkv, d) in BRUTE_SHAPES:
+        q, k, v = _rand(rng, B, nq, hq, d), _rand(rng, B, nk, hkv, d), _rand(rng, B, nk, hkv, d)
+        for window in WINDOW_CASES:
+            for causal in (False, True):
+                o, lse = m.attn_fwd(q, k, v, 0.6, causal, window)
+                ob, lb = _brute_fwd(q, k, v, 0.6, causal, window)
+                np.testing.assert_allclose(o, ob, rtol=0, atol=1e-12)
+                np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(lb))
+                fin = np.isfinite(lb)
+                np.testing.assert_allclose(lse[fin], lb[fin], rtol=0, atol=1e-12)
+
+
+def pin_window_special_cases(m):
+    """(-1, 0) is the causal mask; a band wider than the sequence is no mask;
+    (0, 0) leaves each row its own diagonal key (o = v, LSE = its score)."""
+    rng = np.random.default_rng(22)
+    q, k, v = _rand(rng, 2, 9, 2, 4), _rand(rng, 2, 9, 2, 4), _rand(rng, 2, 9, 2, 4)
+    oc, lc = m.attn_fwd(q, k, v, 0.5, True)
+    ow, lw = m.attn_fwd(q, k, v, 0.5, False, (-1, 0))
+    np.testing.assert_allclose(ow, oc, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lw, lc, rtol=0, atol=1e-14)
+    on, ln_ = m.attn_fwd(q, k, v, 0.5, False)
+    ob, lb = m.attn_fwd(q, k, v, 0.5, False, (9, 9))
+    np.testing.assert_allclose(ob, on, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lb, ln_, rtol=0, atol=1e-14)
+    od, ld = m.attn_fwd(q, k, v, 0.5, False, (0, 0))
+    np.testing.assert_allclose(od, v, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ld, 0.5 * np.einsum("bihc,bihc->bhi", q, k), rtol=0, atol=1e-13)
+
+
+def pin_varlen_is_per_sequence_dense(m):
+    """Each packed sequence is an independent problem: equal to a dense
+    forward of that sequence alone, including Nq != Nk (bottom-right) and
+    empty sequences; and equal-length packing equals the padded batch."""
+    rng = np.random.default_rng(23)
+    lq, lk = [3, 0, 5, 1, 4], [3, 2, 7, 1, 0]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q, k, v = _rand(rng, cu_q[-1], 4, 3), _rand(rng, cu_k[-1], 2, 3), _rand(rng, cu_k[-1], 2, 3)
+    for causal in (False, True):
+        for window in ((-1, -1), (1, 1), (2, 0)):
+            o, lse = m.attn_fwd_varlen(q, k, v, cu_q, cu_k, 0.7, causal, window)
+            for b in range(len(lq)):
+                a, e, c, f = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+                if e == a:
+                    continue
+                ob, lb = _brute_fwd(q[None, a:e], k[None, c:f], v[None, c:f], 0.7, causal, window)
+                np.testing.assert_allclose(o[a:e], ob[0], rtol=0, atol=1e-12)
+                np.testing.assert_array_equal(np.isneginf(lse[:, a:e]), np.isneginf(lb[0]))
+    qb, kb, vb = _rand(rng, 3, 6, 2, 4), _rand(rng, 3, 6, 1, 4), _rand(rng, 3, 6, 1, 4)
+    cu = np.array([0, 6, 12, 18])
+    o, lse = m.attn_fwd_varlen(qb.reshape(18, 2, 4), kb.reshape(18, 1, 4), vb.reshape(18, 1, 4), cu, cu, 0.4, True)
+    od, ld = m.attn_fwd(qb, kb, vb, 0.4, True)
+    np.testing.assert_allclose(o, od.reshape(18, 2, 4), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, ld.transpose(1, 0, 2).reshape(2, 18), rtol=0, atol=1e-14)
+
+
+PINS += [pin_golden_window, pin_golden_varlen, pin_window_brute_force, pin_window_special_cases,
+         pin_varlen_is_per_sequence_dense]
+
+
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_oracle_pin(pin):
     pin(oracle_attention)
@@ -344,8 +438,8 @@ def test_gqa_requires_divisibility():
 MUTANTS = {
     "scale_dropped": ("s = scale * (q @ k.T)", "s = (q @ k.T)"),
     "scores_transposed": ("s = scale * (q @ k.T)", "s = scale * ((q @ k.T).T if q.shape[0] == k.shape[0] else q @ k.T)"),
-    "mask_top_left": ("<= np.asarray(rows)[:, None] + (nk - nq)", "<= np.asarray(rows)[:, None]"),
-    "mask_strict": ("<= np.asarray(rows)[:, None] + (nk - nq)", "< np.asarray(rows)[:, None] + (nk - nq)"),
+    "mask_top_left": ("keep = j <= diag", "keep = j <= np.asarray(rows)[:, None]"),
+    "mask_strict": ("keep = j <= diag", "keep = j < diag"),
     "gqa_modulo": ("kh = h // g\n            _, p, lse_bh", "kh = h % hkv\n            _, p, lse_bh"),
     "lse_without_max": ("m_safe[:, 0] + np.log(np.where", "np.log(np.where"),
     "lse_log2": ("m_safe[:, 0] + np.log(np.where", "m_safe[:, 0] + np.log2(np.where"),
@@ -357,6 +451,11 @@ MUTANTS = {
     "dk_overwrite_group": ("dk[b, :, kh, :] += scale", "dk[b, :, kh, :] = scale"),
     "decode_reads_whole_cache": ("kb = np.asarray(k_cache[b, :n]", "kb = np.asarray(k_cache[b, :]"),
     "decode_value_prefix_off_by_one": ("vb = np.asarray(v_cache[b, :n]", "vb = np.asarray(v_cache[b, 1:n + 1]"),
+    "window_left_strict": ("j >= diag - wl", "j > diag - wl"),
+    "window_sides_swapped": ("j >= diag - wl, s", "j >= diag - wr, s"),
+    "window_top_left": ("diag = np.asarray(rows)[:, None] + (nk - nq)", "diag = np.asarray(rows)[:, None] + 0 * (nk - nq)"),
+    "varlen_keys_from_query_offsets": ("k[None, k0:k1], v[None, k0:k1]", "k[None, q0:q0 + (k1 - k0)], v[None, q0:q0 + (k1 - k0)]"),
+    "varlen_lse_row_major": ("lse[:, q0:q1] = lb[0]", "lse[:, q0:q1] = lb[0][::-1] if lb.shape[1] > 1 else lb[0]"),
 }
 
 
