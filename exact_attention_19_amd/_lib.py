@@ -34,6 +34,8 @@ _SZ = ctypes.c_size_t
 # name -> (restype, argtypes); must match include/fa.h.
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _P]),

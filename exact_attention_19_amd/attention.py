@@ -66,6 +66,56 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     return out, lse
 
 
+def fa_fwd_window(q, k, v, window, scale=None, causal=False):
+    """Sliding-window forward (bf16, d = 128): window = (left, right), -1 is
+    unbounded on that side. Returns (o, lse) laid out as fa_fwd."""
+    _check_tensor("q", q, torch.bfloat16, 4)
+    _check_tensor("k", k, torch.bfloat16, 4, q.device)
+    _check_tensor("v", v, torch.bfloat16, 4, q.device)
+    B, N, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    Hkv = k.shape[2]
+    wl, wr = (int(x) for x in window)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = _lib.load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale,
+                                   int(bool(causal)), wl, wr, _lib.FA_BF16, _stream(q.device))
+    _lib.check(st)
+    return out, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None, causal=False,
+                  window=(-1, -1)):
+    """Forward over packed variable-length sequences (bf16, d = 128).
+
+    q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_seqlens_q/k: int32 [B + 1]
+    device prefix sums. Returns (o [total_q, Hq, d], lse [Hq, total_q])."""
+    _check_tensor("q", q, torch.bfloat16, 3)
+    dev = q.device
+    _check_tensor("k", k, torch.bfloat16, 3, dev)
+    _check_tensor("v", v, torch.bfloat16, 3, dev)
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, torch.int32, 1, dev)
+    _check_tensor("cu_seqlens_k", cu_seqlens_k, torch.int32, 1, dev)
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if k.shape != v.shape or k.shape[2] != d:
+        raise ValueError(f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.numel() - 1
+    wl, wr = (int(x) for x in window)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev)
+    st = _lib.load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), B, int(max_seqlen_q), total_q, total_k, Hq, Hkv, d, scale,
+                                   int(bool(causal)), wl, wr, _lib.FA_BF16, _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
 def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False):
     """Attention backward from the forward's O and LSE. Returns (dq, dk, dv)."""
     _check_tensor("q", q, torch.bfloat16, 4)

@@ -133,6 +133,63 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   return hip_status(fn, fa::launch_fwd(a));
 }
 
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                        int N, int d, float scale, int causal, int window_left, int window_right, int dtype,
+                        void* stream) {
+  static const char* fn = "fa_fwd_window";
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
+  if (window_left < 0 && window_right < 0) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dtype, stream);
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 supports a window", fn);
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: a window needs d = 128 (got %d)", fn, d);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k", k, 16));
+  FA_TRY(check_ptr(fn, "v", v, 16));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  FA_TRY(check_ptr(fn, "lse", lse, 4));
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal ? 1 : 0, dtype,
+                reinterpret_cast<hipStream_t>(stream)};
+  fa::FwdSeq seq;
+  seq.win_left = window_left;
+  seq.win_right = window_right;
+  return hip_status(fn, fa::launch_fwd_seq(a, seq));
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int max_seqlen_q,
+                        int total_q, int total_k, int Hq, int Hkv, int d, float scale, int causal, int window_left,
+                        int window_right, int dtype, void* stream) {
+  static const char* fn = "fa_fwd_varlen";
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, max_seqlen_q, d, scale));
+  if (total_q <= 0 || total_k < 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: total_q %d must be > 0 and total_k %d >= 0", fn, total_q, total_k);
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is supported", fn);
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: d = 128 only (got %d)", fn, d);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k", k, 16));
+  FA_TRY(check_ptr(fn, "v", v, 16));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  FA_TRY(check_ptr(fn, "lse", lse, 4));
+  FA_TRY(check_ptr(fn, "cu_seqlens_q", cu_seqlens_q, 4));
+  FA_TRY(check_ptr(fn, "cu_seqlens_k", cu_seqlens_k, 4));
+  if ((int64_t)(max_seqlen_q + 127) / 128 * B * Hq > 0x7fffffff)
+    return fail(FA_ERR_INVALID_ARG, "%s: launch grid too large", fn);
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, d, scale, causal ? 1 : 0, dtype,
+                reinterpret_cast<hipStream_t>(stream)};
+  fa::FwdSeq seq;
+  seq.cu_q = cu_seqlens_q;
+  seq.cu_k = cu_seqlens_k;
+  seq.total_q = total_q;
+  seq.total_k = total_k;
+  seq.max_q = max_seqlen_q;
+  seq.win_left = window_left;
+  seq.win_right = window_right;
+  return hip_status(fn, fa::launch_fwd_seq(a, seq));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   (void)Hkv;
   (void)d;

@@ -286,11 +286,13 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
 // read from LDS feeds QB MFMAs (one per query block), so LDS read traffic per
 // MFMA falls as 1/QB; with QB = 2 the O accumulators (128 registers) and the
 // Q operands (64) need one wave per SIMD.
-template <int NWAVES, int NSTAGE, int QB, bool CAUSAL>
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
-    int num_q_tiles) {
+    int num_q_tiles, FwdSeq seq) {
+  constexpr bool VARLEN = (MODE & kModeVarlen) != 0;
+  constexpr bool WINDOW = (MODE & kModeWindow) != 0;
   constexpr int D = 128;
   constexpr int WQ = 32 * QB;           // query rows per wave
   constexpr int BM = NWAVES * WQ;       // query rows per workgroup
@@ -324,14 +326,35 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   const int hq = uniform(bh - b * Hq);
   const int hk = uniform(hq / (Hq / Hkv));
 
+  // This sequence: query rows [q_start, q_start + Nq) and key rows
+  // [k_start, k_start + Nk) of the packed tensors (dense: b*N and N). Packed
+  // offsets are clamped to the tensors, so malformed prefix sums cannot read
+  // or write outside them.
+  int q_start, Nq, k_start, Nk;
+  if constexpr (VARLEN) {
+    q_start = uniform(min(max(seq.cu_q[b], 0), seq.total_q));
+    Nq = uniform(min(max(seq.cu_q[b + 1], q_start), seq.total_q)) - q_start;
+    k_start = uniform(min(max(seq.cu_k[b], 0), seq.total_k));
+    Nk = uniform(min(max(seq.cu_k[b + 1], k_start), seq.total_k)) - k_start;
+  } else {
+    q_start = b * N;
+    Nq = N;
+    k_start = b * N;
+    Nk = N;
+  }
+  const int q0 = qt * BM;
+  if (q0 >= Nq) return;  // whole workgroup past this sequence's queries
+  const int off = Nk - Nq;  // bottom-right alignment of the causal mask / window
+  const int wl = WINDOW ? seq.win_left : -1;
+  const int wr = WINDOW ? seq.win_right : -1;
+
   const int64_t q_rs = (int64_t)Hq * D;
   const int64_t kv_rs = (int64_t)Hkv * D;
-  const __bf16* kb = k + ((int64_t)b * N) * kv_rs + (int64_t)hk * D;
-  const __bf16* vb = v + ((int64_t)b * N) * kv_rs + (int64_t)hk * D;
+  const __bf16* kb = k + (int64_t)k_start * kv_rs + (int64_t)hk * D;
+  const __bf16* vb = v + (int64_t)k_start * kv_rs + (int64_t)hk * D;
 
-  const int q0 = qt * BM;
   const int qw0 = q0 + wave * WQ;
-  const bool wave_active = qw0 < N;
+  const bool wave_active = qw0 < Nq;
   int my_q[QB];
 #pragma unroll
   for (int j = 0; j < QB; ++j) my_q[j] = qw0 + 32 * j + l32;
@@ -339,14 +362,19 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   bf16x8 qf[QB][DS];
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
-    const __bf16* qrow = q + ((int64_t)b * N + min(my_q[j], N - 1)) * q_rs + (int64_t)hq * D + 8 * hh;
+    const __bf16* qrow = q + ((int64_t)q_start + min(my_q[j], Nq - 1)) * q_rs + (int64_t)hq * D + 8 * hh;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[j][s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
   }
 
-  int kv_end = N;
-  if (CAUSAL) kv_end = min(N, q0 + BM);
-  const int n_tiles = (kv_end + 63) / 64;
+  // Keys any query of the workgroup can see: [kv_begin, kv_end).
+  const int q_last = min(q0 + BM, Nq) - 1;
+  int kv_begin = 0, kv_end = Nk;
+  if (CAUSAL) kv_end = min(kv_end, q_last + off + 1);
+  if (WINDOW && wr >= 0) kv_end = min(kv_end, q_last + off + wr + 1);
+  if (WINDOW && wl >= 0) kv_begin = max(0, q0 + off - wl);
+  const int t_begin = kv_begin / 64;
+  const int t_end = kv_end > kv_begin ? (kv_end + 63) / 64 : t_begin;
 
   // Per-lane LDS byte offsets inside a tile (constant over the loop).
   // K operand (A of S^T): row 32*kbk + l32, logical unit 2*s + hh.
@@ -380,7 +408,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * 64 * kv_rs * 2;
-    const int nrows = N - t * 64;
+    const int nrows = Nk - t * 64;
     dma_rows64(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, CPW, dma_off);
     dma_rows64(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES, CPW,
                dma_off);
@@ -409,10 +437,20 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     const int base_key = k0 + kbk * 32 + 4 * hh;
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
-      int lim = N - 1 - base_key;
-      if (CAUSAL) lim = min(lim, my_q[j] - base_key);
+      int lim = Nk - 1 - base_key;                     // masked iff c(e) > lim
+      if (CAUSAL) lim = min(lim, my_q[j] + off - base_key);
+      if (WINDOW && wr >= 0) lim = min(lim, my_q[j] + off + wr - base_key);
+      if constexpr (WINDOW) {
+        const int lo = wl >= 0 ? my_q[j] + off - wl - base_key : -1;  // masked iff c(e) < lo
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc.s[j][e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc.s[j][e];
+        for (int e = 0; e < 16; ++e) {
+          const int c = 8 * (e >> 2) + (e & 3);
+          sc.s[j][e] = (c > lim || c < lo) ? kNegInf : sc.s[j][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc.s[j][e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc.s[j][e];
+      }
     }
   };
   // Row maximum of a block in log2 units (max3 tree, then the partner lane).
@@ -557,21 +595,23 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   };
 
   // Tiles are prefetched NSTAGE - 1 ahead into a ring of LDS stages. Step t
-  // (on stage t % NSTAGE, a compile-time constant so LDS offsets are
-  // immediates) issues tile t + NSTAGE - 1 into the stage freed by step
+  // (on stage (t - t_begin) % NSTAGE, a compile-time constant so LDS offsets
+  // are immediates) issues tile t + NSTAGE - 1 into the stage freed by step
   // t - 1, consumes tile t, then waits until tile t + 1 has landed (the
   // DMAs of later tiles may stay in flight) before the workgroup barrier.
-  // Tiles [0, n_full) need no masking for any wave of the workgroup and run
-  // the unmasked body; the rest (causal diagonal, ragged end) run the masked
-  // body in a second loop.
+  // Tiles [f_begin, f_end) need no masking for any query of the workgroup
+  // and run the unmasked body; the rest (causal diagonal, window edges,
+  // ragged end) run the masked body.
   static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three LDS stages");
   constexpr int DMA_PER_STEP = 2 * CPW;  // K and V chunks issued by each wave
   auto step = [&](int t, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
-    const bool more = t + NSTAGE - 1 < n_tiles;
+    const bool more = t + NSTAGE - 1 < t_end;
     if (more) issue(t + NSTAGE - 1, (STG + NSTAGE - 1) % NSTAGE);
     const int k0 = t * 64;
-    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + WQ - 1);
+    bool skip = !wave_active || (CAUSAL && k0 > qw0 + WQ - 1 + off);
+    if (WINDOW && wr >= 0) skip = skip || k0 > qw0 + WQ - 1 + off + wr;
+    if (WINDOW && wl >= 0) skip = skip || k0 + 63 < qw0 + off - wl;
     if (!skip) {
       const unsigned char* ks = smem + STG * STAGE;
       tile(ks, ks + TILE, k0, mask_tag);
@@ -581,38 +621,47 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     barrier_keep_dma();
   };
   auto step_any = [&](int t, auto mask_tag) __attribute__((always_inline)) {
-    const int stg = t % NSTAGE;
+    const int stg = (t - t_begin) % NSTAGE;
     if (stg == 0) step(t, std::integral_constant<int, 0>{}, mask_tag);
     else if (NSTAGE > 1 && stg == 1) step(t, std::integral_constant<int, 1 % NSTAGE>{}, mask_tag);
     else step(t, std::integral_constant<int, 2 % NSTAGE>{}, mask_tag);
   };
-  int n_full = N / 64;
-  if (CAUSAL) n_full = min(n_full, q0 / 64);
-  n_full = min(n_full, n_tiles);
+  // Full tiles: every key of the tile visible to every query of the workgroup.
+  int full_hi = Nk - 1;                                 // last key that may be in a full tile
+  if (CAUSAL) full_hi = min(full_hi, q0 + off);
+  if (WINDOW && wr >= 0) full_hi = min(full_hi, q0 + off + wr);
+  int f_begin = t_begin;
+  if (WINDOW && wl >= 0) f_begin = max(t_begin, (max(q_last + off - wl, 0) + 63) / 64);
+  int f_end = full_hi >= 0 ? (full_hi + 1) / 64 : 0;
+  f_end = max(min(f_end, t_end), f_begin);
+  f_begin = min(f_begin, t_end);
 
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) {
-    if (i < n_tiles) issue(i, i);
+    if (t_begin + i < t_end) issue(t_begin + i, i);
   }
   wait_vmcnt<0>();
   barrier_keep_dma();
-  int t = 0;
-  for (; t + NSTAGE <= n_full; t += NSTAGE) {
+  int t = t_begin;
+  for (; t < f_begin; ++t) step_any(t, std::true_type{});
+  for (; t < f_end && (t - t_begin) % NSTAGE != 0; ++t) step_any(t, std::false_type{});
+  for (; t + NSTAGE <= f_end; t += NSTAGE) {
     step(t, std::integral_constant<int, 0>{}, std::false_type{});
     step(t + 1, std::integral_constant<int, 1 % NSTAGE>{}, std::false_type{});
     if constexpr (NSTAGE == 3) step(t + 2, std::integral_constant<int, 2>{}, std::false_type{});
   }
-  for (; t < n_full; ++t) step_any(t, std::false_type{});
-  for (; t < n_tiles; ++t) step_any(t, std::true_type{});
+  for (; t < f_end; ++t) step_any(t, std::false_type{});
+  for (; t < t_end; ++t) step_any(t, std::true_type{});
 
   if (!wave_active) return;
+  const int64_t lse_base = VARLEN ? (int64_t)hq * seq.total_q + q_start : ((int64_t)b * Hq + hq) * N;
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const float l_tot = pair_sum(l_run[j]);
-    if (my_q[j] < N) {
+    if (my_q[j] < Nq) {
       const bool empty = !(l_tot > 0.f);
       const float inv = empty ? 0.f : 1.f / l_tot;
-      __bf16* orow = o + ((int64_t)b * N + my_q[j]) * q_rs + (int64_t)hq * D;
+      __bf16* orow = o + ((int64_t)q_start + my_q[j]) * q_rs + (int64_t)hq * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -623,7 +672,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * i + 4 * hh) = w;
         }
       }
-      if (hh == 0) lse[((int64_t)b * Hq + hq) * N + my_q[j]] = empty ? kNegInf : (m_run[j] + __log2f(l_tot)) * kLn2;
+      if (hh == 0) lse[lse_base + my_q[j]] = empty ? kNegInf : (m_run[j] + __log2f(l_tot)) * kLn2;
     }
   }
 }
@@ -714,20 +763,21 @@ hipError_t launch_bf16(const FwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int NWAVES, int NSTAGE, int QB, bool CAUSAL>
-hipError_t launch_d128(const FwdArgs& a) {
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE = 0>
+hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   constexpr int BM = NWAVES * 32 * QB;
-  const int num_q_tiles = (a.N + BM - 1) / BM;
+  const int rows = (MODE & kModeVarlen) ? seq.max_q : a.N;
+  const int num_q_tiles = (rows + BM - 1) / BM;
   const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + NWAVES * 4096;  // tile ring + rescale slots
-  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL>;
+  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles);
+                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles, seq);
   return hipGetLastError();
 }
 
@@ -752,6 +802,24 @@ hipError_t launch_fwd(const FwdArgs& a) {
     return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
   }
   return a.causal ? launch_d128<4, 2, 1, true>(a) : launch_d128<4, 2, 1, false>(a);
+}
+
+hipError_t launch_fwd_seq(const FwdArgs& a, const FwdSeq& seq) {
+  const bool varlen = seq.cu_q != nullptr;
+  const bool window = seq.win_left >= 0 || seq.win_right >= 0;
+  if (varlen && window) {
+    return a.causal ? launch_d128<4, 2, 1, true, kModeVarlen | kModeWindow>(a, seq)
+                    : launch_d128<4, 2, 1, false, kModeVarlen | kModeWindow>(a, seq);
+  }
+  if (varlen) {
+    return a.causal ? launch_d128<4, 2, 1, true, kModeVarlen>(a, seq)
+                    : launch_d128<4, 2, 1, false, kModeVarlen>(a, seq);
+  }
+  if (window) {
+    return a.causal ? launch_d128<4, 2, 1, true, kModeWindow>(a, seq)
+                    : launch_d128<4, 2, 1, false, kModeWindow>(a, seq);
+  }
+  return launch_fwd(a);
 }
 
 }  // namespace fa

@@ -23,6 +23,25 @@ struct FwdArgs {
   hipStream_t stream;
 };
 
+// Sequence geometry for the d = 128 bf16 forward beyond dense batches.
+// Varlen: sequences packed along the row axis, cu_q / cu_k are device
+// [B + 1] prefix sums (rows cu_q[b] .. cu_q[b+1] - 1 of Q, O and of the LSE
+// column range; likewise cu_k for K, V); LSE is laid out [Hq, total_q].
+// Window: query i keeps key j iff i + off - win_left <= j <= i + off + win_right,
+// off = Nk - Nq, a negative bound meaning unbounded on that side.
+struct FwdSeq {
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0;
+  int total_k = 0;
+  int max_q = 0;
+  int win_left = -1;
+  int win_right = -1;
+};
+
+constexpr int kModeVarlen = 1;
+constexpr int kModeWindow = 2;
+
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -57,6 +76,9 @@ constexpr int kDecodeDefaultChunk = 512;
 constexpr int kDecodeMaxHeadsPerGroup = 4;
 
 hipError_t launch_fwd(const FwdArgs& a);
+// Varlen and/or windowed forward (bf16, d = 128). a.N is ignored; a.B is
+// the number of sequences.
+hipError_t launch_fwd_seq(const FwdArgs& a, const FwdSeq& seq);
 
 // Backward workspace: D = rowsum(dO * O) at `delta` ([B, Hq, N] float32),
 // then LSE * log2(e) at delta + bwd_vec_stride(...) (same shape).

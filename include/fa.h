@@ -72,6 +72,53 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                  int dtype, void* stream);
 
+/*
+ * Forward pass with a sliding window (sliding-window attention: hysenlabs
+ * digest, `window_size` among the arguments in the outputs section and the
+ * v2.3 entry of the changelog in the constraints section). Query i keeps key
+ * j iff i - window_left <= j <= i + window_right (a side of -1 is unbounded;
+ * causal = 1 additionally keeps only j <= i). With both sides -1 this is
+ * fa_fwd. Layouts, alignment and outputs as fa_fwd.
+ * A row that sees no key has O = 0 and LSE = -inf.
+ * Errors: FA_ERR_INVALID_ARG as fa_fwd, or a window side < -1;
+ *   FA_ERR_UNSUPPORTED for a window with dtype != FA_BF16 or d != 128.
+ */
+fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                        int window_left, int window_right, int dtype, void* stream);
+
+/*
+ * Forward pass over packed variable-length sequences (the "varlen"
+ * functions of the v2.0 changelog entry, hysenlabs digest, constraints
+ * section), optionally causal and/or windowed. The B sequences are packed
+ * along the row axis:
+ *   q, o [total_q, Hq, d] bf16;  k, v [total_k, Hkv, d] bf16;
+ *   lse  [Hq, total_q] float32 out;
+ *   cu_seqlens_q, cu_seqlens_k: device int32 [B + 1] prefix sums of the query
+ *   and key lengths (cu[0] = 0, non-decreasing, cu_q[B] = total_q,
+ *   cu_k[B] = total_k). Sequence b is an independent attention problem on
+ *   rows cu_q[b] .. cu_q[b+1]-1 of q/o and cu_k[b] .. cu_k[b+1]-1 of k/v.
+ * Causal masking and the window are aligned to the bottom-right corner of each
+ *   sequence (v2.1 entry): with Nq, Nk the lengths and off = Nk - Nq, query i
+ *   keeps key j iff j <= i + off (causal) and
+ *   i + off - window_left <= j <= i + off + window_right (a side of -1 is
+ *   unbounded). A row that sees no key (e.g. causal with Nq > Nk) has O = 0,
+ *   LSE = -inf.
+ * max_seqlen_q must be >= every query length: it sizes the launch, and rows of
+ *   a longer sequence past max_seqlen_q are left unwritten. Prefix sums are
+ *   read on the device and clamped to [0, total], so malformed values cannot
+ *   cause accesses outside the tensors (their results are unspecified).
+ * Only d = 128 and FA_BF16. Pointers 16-byte aligned (lse, cu_*: 4-byte).
+ * Errors: FA_ERR_INVALID_ARG for NULL/misaligned pointers, B, Hq, Hkv,
+ *   max_seqlen_q or total_q <= 0, total_k < 0, Hq % Hkv != 0, a bad scale or a
+ *   window side < -1; FA_ERR_UNSUPPORTED for d != 128 or dtype != FA_BF16.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int B, int max_seqlen_q, int total_q, int total_k,
+                        int Hq, int Hkv, int d, float scale, int causal,
+                        int window_left, int window_right, int dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (256-byte aligned). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

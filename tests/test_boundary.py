@@ -87,6 +87,42 @@ def test_bwd_validation(lib):
     assert "fa_bwd" in lib.fa_last_error().decode()
 
 
+def test_window_validation(lib):
+    args = [FAKE] * 5 + [1, 4, 2, 64, 128, 0.1, 0, 3, 0, _lib.FA_BF16, None]
+    bad = list(args)
+    bad[12] = -2  # window_left
+    assert lib.fa_fwd_window(*bad) == _lib.FA_ERR_INVALID_ARG
+    d64 = list(args)
+    d64[9] = 64
+    assert lib.fa_fwd_window(*d64) == _lib.FA_ERR_UNSUPPORTED
+    f32 = list(args)
+    f32[14] = _lib.FA_FP32
+    assert lib.fa_fwd_window(*f32) == _lib.FA_ERR_UNSUPPORTED
+    null_lse = list(args)
+    null_lse[4] = None
+    assert lib.fa_fwd_window(*null_lse) == _lib.FA_ERR_INVALID_ARG
+    assert lib.fa_last_error().decode().startswith("fa_fwd_window")
+
+
+def test_varlen_validation(lib):
+    # q k v o lse cu_q cu_k, B, max_q, total_q, total_k, Hq, Hkv, d, scale, causal, wl, wr, dtype, stream
+    args = [FAKE] * 7 + [3, 100, 200, 150, 4, 2, 128, 0.1, 1, -1, -1, _lib.FA_BF16, None]
+    for idx, val, status in ((7, 0, _lib.FA_ERR_INVALID_ARG),       # B
+                             (8, 0, _lib.FA_ERR_INVALID_ARG),       # max_seqlen_q
+                             (9, 0, _lib.FA_ERR_INVALID_ARG),       # total_q
+                             (10, -1, _lib.FA_ERR_INVALID_ARG),     # total_k
+                             (11, 3, _lib.FA_ERR_INVALID_ARG),      # Hq not a multiple of Hkv
+                             (13, 64, _lib.FA_ERR_UNSUPPORTED),     # d
+                             (17, -5, _lib.FA_ERR_INVALID_ARG),     # window_right
+                             (18, _lib.FA_FP32, _lib.FA_ERR_UNSUPPORTED),
+                             (5, None, _lib.FA_ERR_INVALID_ARG),    # cu_seqlens_q
+                             (6, FAKE + 2, _lib.FA_ERR_INVALID_ARG)):  # misaligned cu_seqlens_k
+        bad = list(args)
+        bad[idx] = val
+        assert lib.fa_fwd_varlen(*bad) == status, (idx, val)
+        assert lib.fa_last_error().decode().startswith("fa_fwd_varlen")
+
+
 def test_decode_validation(lib):
     ws = lib.fa_decode_workspace_bytes(2, 8, 2, 1000, 128, 0)
     args = [FAKE] * 7 + [ws, 2, 8, 2, 1000, 128, 0.1, 0, 0, _lib.FA_BF16, None]

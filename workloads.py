@@ -17,6 +17,7 @@ guide to flash-linear-attention (benchmark section).
 """
 from __future__ import annotations
 
+import itertools
 import math
 from dataclasses import dataclass, field
 
@@ -44,6 +45,21 @@ def prefill_inputs(B, N, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0, with_do=Fal
     if with_do:
         out["do"] = _randn((B, N, Hq, d), gen, 1.0, dt)
     return out
+
+
+def varlen_inputs(lens_q, lens_k, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0):
+    """Packed variable-length sequences: q [sum(lens_q), Hq, d], k/v
+    [sum(lens_k), Hkv, d] drawn in that order, and int32 prefix sums
+    cu_q, cu_k of shape [B + 1]."""
+    dt = DTYPES[dtype]
+    gen = torch.Generator().manual_seed(seed)
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    q = _randn((tq, Hq, d), gen, mult, dt)
+    k = _randn((tk, Hkv, d), gen, mult, dt)
+    v = _randn((tk, Hkv, d), gen, mult, dt)
+    cu_q = torch.tensor([0] + list(itertools.accumulate(int(x) for x in lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(itertools.accumulate(int(x) for x in lens_k)), dtype=torch.int32)
+    return {"q": q, "k": k, "v": v, "cu_q": cu_q, "cu_k": cu_k}
 
 
 def decode_seqlens(B, lo, hi, seed=0):
