@@ -116,8 +116,9 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
     return out, lse
 
 
-def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False):
-    """Attention backward from the forward's O and LSE. Returns (dq, dk, dv)."""
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1)):
+    """Attention backward from the forward's O and LSE. Returns (dq, dk, dv).
+    A window other than (-1, -1) calls fa_bwd_window (d = 128)."""
     _check_tensor("q", q, torch.bfloat16, 4)
     dev = q.device
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -134,8 +135,14 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False):
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                    _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16, _stream(dev))
+    wl, wr = (int(x) for x in window)
+    if wl < 0 and wr < 0:
+        st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16, _stream(dev))
+    else:
+        st = lib.fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), wl, wr,
+                               _lib.FA_BF16, _stream(dev))
     _lib.check(st)
     return dq, dk, dv
 

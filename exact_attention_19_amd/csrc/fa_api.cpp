@@ -78,9 +78,13 @@ void decode_ws_layout(int B, int Hq, int N, int d, int num_splits, int* chunk, i
 fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     int dtype, void* stream) {
+                     int dtype, void* stream, int window_left = -1, int window_right = -1) {
   FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
   if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  if (window_left < -1 || window_right < -1)
+    return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
+  if ((window_left >= 0 || window_right >= 0) && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "%s: a window needs d = 128 (got %d)", fn, d);
   const bool all = stage < 0;
   if (all || stage == 0) {
     FA_TRY(check_ptr(fn, "o", o, 16));
@@ -105,7 +109,7 @@ fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, co
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
-                reinterpret_cast<hipStream_t>(stream)};
+                reinterpret_cast<hipStream_t>(stream), window_left, window_right};
   float* delta = static_cast<float*>(workspace);
   return hip_status(fn, all ? fa::launch_bwd(a, delta) : fa::launch_bwd_stage(a, delta, stage));
 }
@@ -210,6 +214,14 @@ fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, c
   if (stage < 0 || stage > 2) return fail(FA_ERR_INVALID_ARG, "fa_bwd_stage: stage %d is not 0, 1 or 2", stage);
   return bwd_common("fa_bwd_stage", stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq,
                     Hkv, N, d, scale, causal, dtype, stream);
+}
+
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, int window_left,
+                        int window_right, int dtype, void* stream) {
+  return bwd_common("fa_bwd_window", -1, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                    N, d, scale, causal, dtype, stream, window_left, window_right);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits) {

@@ -491,13 +491,17 @@ __device__ __forceinline__ int row_offset(int lane) {
 // keys k0 + 32w .. +31 (K, V fragments and dK^T, dV^T accumulators in
 // registers) and sweeps the visible 64-row query tiles of every query head
 // in the GQA group.
-template <bool CAUSAL>
+template <bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
-    float scale_log2) {
+    float scale_log2, int win_left, int win_right) {
   constexpr int D = 128, DS = 8, DB = 4, BQ = 64, BKV = 128;
+  // Key j is visible to query i iff j <= i (causal), i - wl <= j <= i + wr
+  // (window, a negative side unbounded) and both are < N.
+  const int wl = WINDOW ? win_left : -1;
+  const int wr = WINDOW ? win_right : -1;
   constexpr int TILE = 64 * 256;
   constexpr int VEC_OFF = 2 * TILE;            // lse2 (64 floats) then delta (64 floats)
   constexpr int STAGE = 2 * TILE + 512;
@@ -543,16 +547,28 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 
   // Query tiles of each head in the group, in two phases: first every tile
   // that needs masking for some wave of the workgroup (the causal diagonal,
-  // q0 < k0 + BKV - 1, and a ragged last tile), for all heads; then all
-  // full tiles. Each phase is a loop with its own body, so the full tiles
-  // run a branch-free body.
+  // the window's edges, a ragged last tile), for all heads; then all full
+  // tiles. Each phase is a loop with its own body, so the full tiles run a
+  // branch-free body. Per head the visited tiles are [qlo, qhi), the full
+  // ones [f_lo, f_hi).
   const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-  const int m_hi = CAUSAL ? min(nqt, qt0 + (BKV + BQ - 2) / BQ + 1) : qt0;  // diagonal tiles [qt0, m_hi)
-  const bool ragged_extra = (N % BQ != 0) && (nqt - 1 >= m_hi);
-  const int n_m = (m_hi - qt0) + (ragged_extra ? 1 : 0);                    // masked tiles per head
-  const int u_hi = nqt - (ragged_extra ? 1 : 0);
-  const int n_u = u_hi - m_hi;                                               // full tiles per head
+  const int k_last = k0 + BKV - 1;
+  int q_lo_row = 0, q_hi_row = N - 1;  // queries that see some key of the workgroup
+  if (CAUSAL) q_lo_row = k0;
+  if (WINDOW && wr >= 0) q_lo_row = max(q_lo_row, k0 - wr);
+  if (WINDOW && wl >= 0) q_hi_row = min(q_hi_row, k_last + wl);
+  const int qlo = min(max(q_lo_row, 0), N) / BQ;
+  const int qhi = q_hi_row >= max(q_lo_row, 0) ? q_hi_row / BQ + 1 : qlo;
+  int f_lo = qlo, f_hi = qhi;
+  if (CAUSAL) f_lo = max(f_lo, (k_last + BQ - 1) / BQ);
+  if (WINDOW && wr >= 0) f_lo = max(f_lo, (max(k_last - wr, 0) + BQ - 1) / BQ);
+  if (WINDOW && wl >= 0) f_hi = min(f_hi, k0 + wl - (BQ - 1) >= 0 ? (k0 + wl - (BQ - 1)) / BQ + 1 : 0);
+  if (N % BQ != 0) f_hi = min(f_hi, nqt - 1);
+  f_lo = min(f_lo, qhi);
+  f_hi = max(f_hi, f_lo);
+  const int n_lo = f_lo - qlo;
+  const int n_m = n_lo + (qhi - f_hi);  // masked tiles per head
+  const int n_u = f_hi - f_lo;          // full tiles per head
   const int n1 = G * n_m;
   const int n_iter = n1 + G * n_u;
   // Iteration it -> (query head, first query row).
@@ -560,12 +576,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     if (it < n1) {
       const int h = uniform(it / n_m), j = it - h * n_m;
       hq = hk * G + h;
-      q0 = (j < m_hi - qt0 ? qt0 + j : nqt - 1) * BQ;
+      q0 = (j < n_lo ? qlo + j : f_hi + (j - n_lo)) * BQ;
     } else {
       const int i2 = it - n1;
       const int h = uniform(i2 / n_u), j = i2 - h * n_u;
       hq = hk * G + h;
-      q0 = (m_hi + j) * BQ;
+      q0 = (f_lo + j) * BQ;
     }
   };
 
@@ -617,12 +633,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   // branch on diagonal and ragged tiles only.
   auto apply_mask = [&](Scores& sc, int q0, int qb) __attribute__((always_inline)) {
     const int qbase = q0 + 32 * qb + 4 * hh;
-    const int lo = CAUSAL ? my_key - qbase - 1 : -1;  // masked iff c(e) <= lo
-    const int hi = N - qbase;                          // masked iff c(e) >= hi
+    int lo = CAUSAL ? my_key - qbase : -1;                        // masked iff c(e) < lo
+    if (WINDOW && wr >= 0) lo = max(lo, my_key - wr - qbase);
+    int hi = N - 1 - qbase;                                       // masked iff c(e) > hi
+    if (WINDOW && wl >= 0) hi = min(hi, my_key + wl - qbase);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int c = 8 * (e >> 2) + (e & 3);
-      sc.s[e] = (c <= lo || c >= hi) ? kNegInf : sc.s[e];
+      sc.s[e] = (c < lo || c > hi) ? kNegInf : sc.s[e];
     }
   };
   auto algebra = [&](const unsigned char* st, int qb, const Scores& sc) __attribute__((always_inline)) {
@@ -677,7 +695,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     if (it + 1 < n_iter) issue(it + 1, STG ^ 1);
     int hq_unused, q0;
     tile_of(it, hq_unused, q0);
-    const bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
+    bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
+    if (WINDOW && wr >= 0) skip = skip || q0 + BQ - 1 < kw0 - wr;
+    if (WINDOW && wl >= 0) skip = skip || q0 > kw0 + 31 + wl;
     if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag);
     wait_vmcnt<0>();
     barrier_keep_dma();
@@ -720,11 +740,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 
 // dQ for d = 128: one workgroup per (b, query head, 128 query rows), shaped
 // like the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
-template <bool CAUSAL>
+template <bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
-    __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles) {
+    __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles,
+    int win_left, int win_right) {
   constexpr int D = 128, DS = 8, DB = 4, BM = 128, BN = 64;
   constexpr int TILE = 64 * 256;
   constexpr int STAGE = 2 * TILE;  // K tile then V tile
@@ -772,9 +793,25 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     my_dlt = delta[((int64_t)b * Hq + hq) * N + row];
   }
 
-  int kv_end = N;
-  if (CAUSAL) kv_end = min(N, q0 + BM);
-  const int n_tiles = (kv_end + BN - 1) / BN;
+  // Keys any query of the workgroup can see: [kv_begin, kv_end); key j is
+  // visible to query i iff j <= i (causal) and i - wl <= j <= i + wr (window,
+  // a negative side unbounded).
+  const int wl = WINDOW ? win_left : -1;
+  const int wr = WINDOW ? win_right : -1;
+  const int q_last = min(q0 + BM, N) - 1;
+  int t_begin = 0, t_end;
+  if constexpr (!WINDOW) {
+    int kv_end = N;
+    if (CAUSAL) kv_end = min(N, q0 + BM);
+    t_end = (kv_end + BN - 1) / BN;
+  } else {
+    int kv_begin = 0, kv_end = N;
+    if (CAUSAL) kv_end = min(kv_end, q_last + 1);
+    if (wr >= 0) kv_end = min(kv_end, q_last + wr + 1);
+    if (wl >= 0) kv_begin = max(0, q0 - wl);
+    t_begin = kv_begin / BN;
+    t_end = kv_end > kv_begin ? (kv_end + BN - 1) / BN : t_begin;
+  }
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
@@ -815,6 +852,16 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     const int base_key = k0 + kbk * 32 + 4 * hh;
     int lim = N - 1 - base_key;
     if (CAUSAL) lim = min(lim, my_q - base_key);
+    if (WINDOW && wr >= 0) lim = min(lim, my_q + wr - base_key);
+    if constexpr (WINDOW) {
+      const int lo = wl >= 0 ? my_q - wl - base_key : -1;  // masked iff c(e) < lo
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int c = 8 * (e >> 2) + (e & 3);
+        sc.s[e] = (c > lim || c < lo) ? kNegInf : sc.s[e];
+      }
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) sc.s[e] = (8 * (e >> 2) + (e & 3) > lim) ? kNegInf : sc.s[e];
   };
@@ -879,28 +926,57 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   // tile t, waits for its own DMAs and meets the other waves at the barrier.
   auto step = [&](int t, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (t + 1 < n_tiles) issue(t + 1, STG ^ 1);
+    if (t + 1 < t_end) issue(t + 1, STG ^ 1);
     const int k0 = t * BN;
-    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
+    if (WINDOW && wr >= 0) skip = skip || k0 > qw0 + 31 + wr;
+    if (WINDOW && wl >= 0) skip = skip || k0 + BN - 1 < qw0 - wl;
     if (!skip) tile_body(smem + STG * STAGE, k0, mask_tag);
     wait_vmcnt<0>();
     barrier_keep_dma();
   };
-  int n_full = N / BN;
-  if (CAUSAL) n_full = min(n_full, q0 / BN);
-  n_full = min(n_full, n_tiles);
-
-  issue(0, 0);
-  wait_vmcnt<0>();
-  barrier_keep_dma();
-  int t = 0;
-  for (; t + 1 < n_full; t += 2) {
-    step(t, std::integral_constant<int, 0>{}, std::false_type{});
-    step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
-  }
-  for (; t < n_tiles; ++t) {
-    if ((t & 1) == 0) step(t, std::integral_constant<int, 0>{}, std::true_type{});
-    else step(t, std::integral_constant<int, 1>{}, std::true_type{});
+  auto step_any = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    if ((((WINDOW ? t - t_begin : t)) & 1) == 0) step(t, std::integral_constant<int, 0>{}, mask_tag);
+    else step(t, std::integral_constant<int, 1>{}, mask_tag);
+  };
+  if constexpr (!WINDOW) {
+    // Tiles [0, n_full) need no mask for any query of the workgroup.
+    int n_full = N / BN;
+    if (CAUSAL) n_full = min(n_full, q0 / BN);
+    n_full = min(n_full, t_end);
+    issue(0, 0);
+    wait_vmcnt<0>();
+    barrier_keep_dma();
+    int t = 0;
+    for (; t + 1 < n_full; t += 2) {
+      step(t, std::integral_constant<int, 0>{}, std::false_type{});
+      step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    for (; t < t_end; ++t) step_any(t, std::true_type{});
+  } else {
+    // Tiles [f_begin, f_end) are visible in full to every query of the
+    // workgroup and run the unmasked body; the window's edges run the masked
+    // one (which is also correct on full tiles and takes the single steps
+    // that align or end the unrolled loop).
+    int full_hi = N - 1;
+    if (CAUSAL) full_hi = min(full_hi, q0);
+    if (wr >= 0) full_hi = min(full_hi, q0 + wr);
+    int f_begin = t_begin;
+    if (wl >= 0) f_begin = max(t_begin, (max(q_last - wl, 0) + BN - 1) / BN);
+    int f_end = full_hi >= 0 ? (full_hi + 1) / BN : 0;
+    f_end = max(min(f_end, t_end), f_begin);
+    f_begin = min(f_begin, t_end);
+    if (t_begin < t_end) issue(t_begin, 0);
+    wait_vmcnt<0>();
+    barrier_keep_dma();
+    int t = t_begin;
+    for (; t < f_begin; ++t) step_any(t, std::true_type{});
+    if (t < f_end && ((t - t_begin) & 1)) step_any(t++, std::true_type{});
+    for (; t + 1 < f_end; t += 2) {
+      step(t, std::integral_constant<int, 0>{}, std::false_type{});
+      step(t + 1, std::integral_constant<int, 1>{}, std::false_type{});
+    }
+    for (; t < t_end; ++t) step_any(t, std::true_type{});
   }
 
   if (!wave_active || my_q >= N) return;
@@ -923,7 +999,7 @@ hipError_t set_smem(K kern, size_t bytes) {
                              (int)bytes);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW = false>
 hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const float scale_log2 = a.scale * kLog2e;
   float* lse2 = delta + bwd_vec_stride(a.B, a.Hq, a.N);
@@ -940,14 +1016,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
     const int64_t grid = (int64_t)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     if (D == 128) {
-      auto kern = bwd_dkdv_d128_kernel<CAUSAL>;
+      auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW>;
       constexpr size_t smem = 2 * (2 * 64 * 256 + 512);
       hipError_t e = set_smem(kern, smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
                          (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
-                         scale_log2);
+                         scale_log2, a.win_left, a.win_right);
       return hipGetLastError();
     }
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
@@ -963,13 +1039,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const int64_t grid = (int64_t)nqt * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (D == 128) {
-    auto kern = bwd_dq_d128_kernel<CAUSAL>;
+    auto kern = bwd_dq_d128_kernel<CAUSAL, WINDOW>;
     constexpr size_t smem = 2 * 2 * 64 * 256;
     hipError_t e = set_smem(kern, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
-                       (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
+                       (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt,
+                       a.win_left, a.win_right);
     return hipGetLastError();
   }
   auto kern = bwd_dq_kernel<D, CAUSAL>;
@@ -985,6 +1062,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
 
 hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage) {
   if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a, delta, stage) : launch_bwd_t<64, false>(a, delta, stage);
+  if (a.win_left >= 0 || a.win_right >= 0) {
+    return a.causal ? launch_bwd_t<128, true, true>(a, delta, stage) : launch_bwd_t<128, false, true>(a, delta, stage);
+  }
   return a.causal ? launch_bwd_t<128, true>(a, delta, stage) : launch_bwd_t<128, false>(a, delta, stage);
 }
 

@@ -56,6 +56,8 @@ struct BwdArgs {
   float scale;
   int causal;
   hipStream_t stream;
+  int win_left = -1;   // sliding window (d = 128 only); -1 = unbounded side
+  int win_right = -1;
 };
 
 struct DecodeArgs {

@@ -155,6 +155,22 @@ fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, c
                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                        int dtype, void* stream);
 
+/*
+ * Backward pass of the sliding-window forward (fa_fwd_window): the same
+ * gradients as fa_bwd with attention restricted to the band
+ * i - window_left <= j <= i + window_right (a side of -1 is unbounded;
+ * causal additionally keeps j <= i). Deterministic: no atomics, every sum is
+ * taken in a fixed order (the deterministic backward of the v2.4 changelog
+ * entry, hysenlabs digest, constraints section, holds for every backward
+ * here). Arguments, layouts, workspace and errors as fa_bwd, plus
+ * FA_ERR_INVALID_ARG for a window side < -1 and FA_ERR_UNSUPPORTED for a
+ * window with d != 128. With both sides -1 this is fa_bwd.
+ */
+fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
+                        int causal, int window_left, int window_right, int dtype, void* stream);
+
 /* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it). */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
 

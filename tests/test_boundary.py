@@ -104,6 +104,17 @@ def test_window_validation(lib):
     assert lib.fa_last_error().decode().startswith("fa_fwd_window")
 
 
+def test_bwd_window_validation(lib):
+    args = [FAKE] * 10 + [1 << 20, 1, 4, 2, 64, 128, 0.1, 1, 16, 0, _lib.FA_BF16, None]
+    bad = list(args)
+    bad[18] = -3  # window_left
+    assert lib.fa_bwd_window(*bad) == _lib.FA_ERR_INVALID_ARG
+    d64 = list(args)
+    d64[15] = 64
+    assert lib.fa_bwd_window(*d64) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_error().decode().startswith("fa_bwd_window")
+
+
 def test_varlen_validation(lib):
     # q k v o lse cu_q cu_k, B, max_q, total_q, total_k, Hq, Hkv, d, scale, causal, wl, wr, dtype, stream
     args = [FAKE] * 7 + [3, 100, 200, 150, 4, 2, 128, 0.1, 1, -1, -1, _lib.FA_BF16, None]

@@ -124,3 +124,35 @@ def test_varlen_rows_past_max_seqlen_are_not_written():
     ro, _ = oracle.attn_fwd_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_q"].numpy(),
                                    inp["cu_k"].numpy(), 1 / math.sqrt(128), False)
     assert_bf16_close(o[:100 + 256].cpu(), ro[:100 + 256], "O of launched rows")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [(0, 0), (64, 0), (100, 37), (-1, 5), (7, -1), (200, 200)],
+                         ids=["w0_0", "w64_0", "w100_37", "winf_5", "w7_inf", "w200_200"])
+def test_window_backward(window, causal):
+    fa = need_gpu()
+    B, N, Hq, Hkv, d = 1, 333, 4, 2, 128
+    announce(f"bwd window {window} causal={causal} N{N}")
+    inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=37, with_do=True)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_window(q, k, v, window, causal=causal)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal, window=window)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv, _ = oracle.attn_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]),
+                                       1 / math.sqrt(d), causal, window)
+    assert_bf16_close(dq.cpu(), rdq, "dQ")
+    assert_bf16_close(dk.cpu(), rdk, "dK")
+    assert_bf16_close(dv.cpu(), rdv, "dV")
+
+
+def test_window_backward_deterministic():
+    fa = need_gpu()
+    announce("bwd window determinism")
+    inp = workloads.prefill_inputs(1, 700, 8, 2, 128, "bf16", seed=38, with_do=True)
+    q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_window(q, k, v, (128, 0), causal=True)
+    r1 = fa.fa_bwd(q, k, v, o, do, lse, causal=True, window=(128, 0))
+    r2 = fa.fa_bwd(q, k, v, o, do, lse, causal=True, window=(128, 0))
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
