@@ -36,6 +36,13 @@ What is computed, and where the pages define it:
 * Decode with a KV cache (hysenlabs digest, ``flash_attn_with_kvcache``): one
   query row per (sequence, head) attends keys 0 .. L_b - 1 of its cache
   (with one query the bottom-right causal mask keeps every cached key).
+  The same function updates k_cache / v_cache in place (outputs section),
+  and the v2.5 changelog entry adds a paged KV cache. The readings taken:
+  with new rows k_new, v_new ([B, Hkv, d], one token per sequence) the token
+  is written at row L_b and attention covers rows 0 .. L_b; a paged cache is
+  a pool of pages [P, page_size, Hkv, d] and a block table [B, max_pages]
+  maps logical row t of sequence b to row t % page_size of page
+  table[b, t // page_size].
 
 * Sliding window (hysenlabs digest: ``window_size`` among the arguments in
   "出力と運用記録", sliding-window attention in the v2.3 entry of
@@ -222,6 +229,46 @@ def attn_fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, window=(-1,
         o[q0:q1] = ob[0]
         lse[:, q0:q1] = lb[0]
     return o, lse
+
+
+def gather_paged(pages, block_table, b: int, n: int):
+    """Logical rows 0 .. n-1 of sequence b from a paged cache: row t is row
+    t % page_size of page block_table[b, t // page_size]."""
+    page_size = pages.shape[1]
+    t = np.arange(n)
+    return pages[np.asarray(block_table)[b, t // page_size], t % page_size]
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, cache_seqlens, scale: float, k_new=None, v_new=None):
+    """Decode against a paged cache, optionally appending one new token.
+
+    q: [B, Hq, d]; k_pages, v_pages: [P, page_size, Hkv, d];
+    block_table: [B, max_pages] ints; cache_seqlens: [B]. With k_new/v_new
+    ([B, Hkv, d]) the new token is written at logical row L_b of copies of
+    the caches and attention covers L_b + 1 rows. Returns (o [B, Hq, d],
+    lse [B, Hq], k_pages', v_pages') with the updated copies.
+    """
+    k_pages = np.array(k_pages, dtype=np.float64)
+    v_pages = np.array(v_pages, dtype=np.float64)
+    page_size = k_pages.shape[1]
+    table = np.asarray(block_table)
+    lens = np.asarray(cache_seqlens).astype(np.int64)
+    if k_new is not None:
+        for b in range(len(lens)):
+            t = int(lens[b])
+            pg, r = table[b, t // page_size], t % page_size
+            k_pages[pg, r] = np.asarray(k_new[b], dtype=np.float64)
+            v_pages[pg, r] = np.asarray(v_new[b], dtype=np.float64)
+        lens = lens + 1
+    b_ = len(lens)
+    n_max = int(lens.max())
+    kc = np.zeros((b_, n_max) + k_pages.shape[2:])
+    vc = np.zeros_like(kc)
+    for b in range(b_):
+        kc[b, :lens[b]] = gather_paged(k_pages, table, b, int(lens[b]))
+        vc[b, :lens[b]] = gather_paged(v_pages, table, b, int(lens[b]))
+    o, lse = attn_decode(q, kc, vc, lens, scale)
+    return o, lse, k_pages, v_pages
 
 
 def attn_fwd_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):

@@ -410,8 +410,57 @@ def pin_varlen_is_per_sequence_dense(m):
     np.testing.assert_allclose(lse, ld.transpose(1, 0, 2).reshape(2, 18), rtol=0, atol=1e-14)
 
 
+def pin_golden_decode_paged(m):
+    data = json.load(open(GOLDEN))
+    for case in data["decode_paged"]:
+        args = (_arr(case["q"]), _arr(case["k_pages"]), _arr(case["v_pages"]), np.array(case["block_table"]),
+                np.array(case["cache_seqlens"]), _expr(case["scale"]))
+        o, lse, kp, vp = m.attn_decode_paged(*args)
+        np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13, err_msg=case["name"])
+        np.testing.assert_allclose(lse, _arr(case["lse"]), rtol=0, atol=1e-13, err_msg=case["name"])
+        ap = case["append"]
+        o, lse, kp, vp = m.attn_decode_paged(*args, _arr(ap["k_new"]), _arr(ap["v_new"]))
+        np.testing.assert_allclose(o, _arr(ap["o"]), rtol=0, atol=1e-13, err_msg=case["name"] + " append")
+        np.testing.assert_allclose(lse, _arr(ap["lse"]), rtol=0, atol=1e-13, err_msg=case["name"] + " append")
+        assert vp[ap["page"], ap["row"], 0, 0] == _arr(ap["v_new"])[0, 0, 0]
+        changed = np.argwhere(vp != _arr(case["v_pages"]))
+        assert [tuple(x[:2]) for x in changed] == [(ap["page"], ap["row"])]
+
+
+def pin_paged_decode_properties(m):
+    """An identity block table is the contiguous cache; a shuffled table gives
+    the same result as the rows it names; appending equals pre-writing the
+    row and decoding one row longer."""
+    rng = np.random.default_rng(24)
+    B, Hq, Hkv, d, ps, mp = 3, 4, 2, 5, 4, 6
+    lens = np.array([1, 13, 23])
+    q = _rand(rng, B, Hq, d)
+    kc, vc = _rand(rng, B, mp * ps, Hkv, d), _rand(rng, B, mp * ps, Hkv, d)
+    ident = np.arange(B * mp).reshape(B, mp)
+    kp, vp = kc.reshape(B * mp, ps, Hkv, d), vc.reshape(B * mp, ps, Hkv, d)
+    o, lse, _, _ = m.attn_decode_paged(q, kp, vp, ident, lens, 0.3)
+    od, ld = m.attn_decode(q, kc, vc, lens, 0.3)
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, ld, rtol=0, atol=1e-14)
+    perm = rng.permutation(B * mp)
+    inv = np.argsort(perm)
+    table = inv[ident]  # logical page p of seq b lives at physical page inv[b*mp + p]
+    o2, l2, _, _ = m.attn_decode_paged(q, kp[perm], vp[perm], table, lens, 0.3)
+    np.testing.assert_allclose(o2, od, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l2, ld, rtol=0, atol=1e-14)
+    kn, vn = _rand(rng, B, Hkv, d), _rand(rng, B, Hkv, d)
+    o3, l3, kp3, vp3 = m.attn_decode_paged(q, kp[perm], vp[perm], table, lens, 0.3, kn, vn)
+    kc4, vc4 = kc.copy(), vc.copy()
+    for b in range(B):
+        kc4[b, lens[b]], vc4[b, lens[b]] = kn[b], vn[b]
+    o4, l4 = m.attn_decode(q, kc4, vc4, lens + 1, 0.3)
+    np.testing.assert_allclose(o3, o4, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l3, l4, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(kp3[inv].reshape(B, mp * ps, Hkv, d), kc4)
+
+
 PINS += [pin_golden_window, pin_golden_varlen, pin_window_brute_force, pin_window_special_cases,
-         pin_varlen_is_per_sequence_dense]
+         pin_varlen_is_per_sequence_dense, pin_golden_decode_paged, pin_paged_decode_properties]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -455,6 +504,10 @@ MUTANTS = {
     "window_sides_swapped": ("j >= diag - wl, s", "j >= diag - wr, s"),
     "window_top_left": ("diag = np.asarray(rows)[:, None] + (nk - nq)", "diag = np.asarray(rows)[:, None] + 0 * (nk - nq)"),
     "varlen_keys_from_query_offsets": ("k[None, k0:k1], v[None, k0:k1]", "k[None, q0:q0 + (k1 - k0)], v[None, q0:q0 + (k1 - k0)]"),
+    "paged_row_within_page": ("return pages[np.asarray(block_table)[b, t // page_size], t % page_size]",
+                              "return pages[np.asarray(block_table)[b, t // page_size], (t + 1) % page_size]"),
+    "paged_append_before_last_row": ("            t = int(lens[b])\n", "            t = int(lens[b]) - 1\n"),
+    "paged_append_not_attended": ("        lens = lens + 1\n", "        lens = lens + 0\n"),
     "varlen_lse_row_major": ("lse[:, q0:q1] = lb[0]", "lse[:, q0:q1] = lb[0][::-1] if lb.shape[1] > 1 else lb[0]"),
 }
 
