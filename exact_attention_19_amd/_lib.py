@@ -42,6 +42,8 @@ SIGNATURES = {
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "fa_decode_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_decode_kvcache_ext": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F,
+                                   _I, _I, _I, _P]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_version": (ctypes.c_char_p, []),
 }

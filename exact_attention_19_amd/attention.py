@@ -176,3 +176,51 @@ def fa_decode_kvcache(q, k_cache, v_cache, cache_seqlens, scale=None, causal=Fal
                                int(num_splits), _lib.FA_BF16, _stream(dev))
     _lib.check(st)
     return out, lse
+
+
+def fa_decode_kvcache_ext(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None, v_new=None, scale=None,
+                          num_splits=0):
+    """Decode with an optional in-place append (k_new, v_new: [B, Hkv, d]) and
+    an optional paged cache (k_cache, v_cache: [num_pages, page_size, Hkv, d],
+    block_table: int32 [B, max_pages]). Returns (o [B, Hq, d], lse [B, Hq])."""
+    _check_tensor("q", q, torch.bfloat16, 3)
+    dev = q.device
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
+    _check_tensor("cache_seqlens", cache_seqlens, torch.int32, 1, dev)
+    B, Hq, d = q.shape
+    if k_cache.shape != v_cache.shape or k_cache.shape[3] != d or cache_seqlens.shape[0] != B:
+        raise ValueError("inconsistent shapes for fa_decode_kvcache_ext")
+    Hkv = k_cache.shape[2]
+    if block_table is not None:
+        _check_tensor("block_table", block_table, torch.int32, 2, dev)
+        if block_table.shape[0] != B:
+            raise ValueError("block_table must be [B, max_pages]")
+        num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+        max_pages = block_table.shape[1]
+        cap = max_pages * page_size
+        rows = 0
+    else:
+        if k_cache.shape[0] != B:
+            raise ValueError("a contiguous cache must be [B, rows, Hkv, d]")
+        num_pages = page_size = max_pages = 0
+        rows = cap = k_cache.shape[1]
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None:
+        _check_tensor("k_new", k_new, torch.bfloat16, 3, dev)
+        _check_tensor("v_new", v_new, torch.bfloat16, 3, dev)
+        if tuple(k_new.shape) != (B, Hkv, d) or k_new.shape != v_new.shape:
+            raise ValueError("k_new/v_new must be [B, Hkv, d]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = _lib.load()
+    ws_bytes = lib.fa_decode_workspace_bytes(B, Hq, Hkv, cap, d, num_splits)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    st = lib.fa_decode_kvcache_ext(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(block_table),
+                                   max_pages, num_pages, page_size, _ptr(k_new), _ptr(v_new), _ptr(o), _ptr(lse),
+                                   _ptr(ws), ws_bytes, B, Hq, Hkv, rows, d, scale, 0, int(num_splits),
+                                   _lib.FA_BF16, _stream(dev))
+    _lib.check(st)
+    return o, lse

@@ -261,4 +261,63 @@ fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_ca
   return hip_status(fn, fa::launch_decode(a, part_o, part_lse, chunk, nsplit));
 }
 
+fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                                const int32_t* block_table, int max_pages_per_seq, int num_pages, int page_size,
+                                const void* k_new, const void* v_new, void* o, float* lse, void* workspace,
+                                size_t workspace_bytes, int B, int Hq, int Hkv, int cache_rows, int d, float scale,
+                                int causal, int num_splits, int dtype, void* stream) {
+  static const char* fn = "fa_decode_kvcache_ext";
+  (void)causal;  // one query aligned to the bottom-right corner sees every cached key
+  int N = cache_rows;
+  int shift = 0;
+  if (block_table) {
+    if (page_size < 16 || (page_size & (page_size - 1)) != 0)
+      return fail(FA_ERR_INVALID_ARG, "%s: page_size %d must be a power of two >= 16", fn, page_size);
+    if (max_pages_per_seq <= 0 || num_pages <= 0)
+      return fail(FA_ERR_INVALID_ARG, "%s: max_pages_per_seq %d and num_pages %d must be > 0", fn,
+                  max_pages_per_seq, num_pages);
+    if ((int64_t)max_pages_per_seq * page_size > 0x7fffffff)
+      return fail(FA_ERR_INVALID_ARG, "%s: max_pages_per_seq * page_size overflows", fn);
+    N = max_pages_per_seq * page_size;
+    while ((1 << shift) < page_size) ++shift;
+  }
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(FA_ERR_INVALID_ARG, "%s: k_new and v_new must be given together", fn);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k_cache", k_cache, 16));
+  FA_TRY(check_ptr(fn, "v_cache", v_cache, 16));
+  FA_TRY(check_ptr(fn, "cache_seqlens", cache_seqlens, 4));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  if (block_table && !aligned(block_table, 4)) return fail(FA_ERR_INVALID_ARG, "%s: block_table misaligned", fn);
+  if (k_new) {
+    FA_TRY(check_ptr(fn, "k_new", k_new, 16));
+    FA_TRY(check_ptr(fn, "v_new", v_new, 16));
+  }
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
+  int chunk, nsplit;
+  size_t ob, lb;
+  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
+  if (block_table && chunk > fa::kDecodeDefaultChunk)
+    return fail(FA_ERR_INVALID_ARG, "%s: with a paged cache num_splits must be 0 or >= %d", fn,
+                (N + fa::kDecodeDefaultChunk - 1) / fa::kDecodeDefaultChunk);
+  if (!workspace || workspace_bytes < ob + lb)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ob + lb,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ob);
+  fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
+                   reinterpret_cast<hipStream_t>(stream)};
+  a.block_table = block_table;
+  a.page_shift = shift;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, chunk, nsplit));
+}
+
 }  // extern "C"

@@ -36,28 +36,77 @@ struct DecSmem {
   static constexpr int BYTES = NSTATE * GP * (D + 2) * 4;
 };
 
-template <int D, int GP>
+// Paged-cache geometry for the split kernel (unused for a contiguous cache).
+struct PageMap {
+  const int32_t* table;  // [B, max_pages]
+  int shift;             // log2(page_size)
+  int max_pages;
+  int num_pages;
+};
+
+// In-place append (flash_attn_with_kvcache updates k_cache / v_cache in
+// place: hysenlabs digest, outputs section): row seqlens[b] of sequence b
+// receives k_new[b], v_new[b]; positions outside [0, N) are skipped. One
+// thread copies 16 bytes of one (b, kv head) row of K and of V.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void decode_append_kernel(
+    __bf16* __restrict__ kc, __bf16* __restrict__ vc, const __bf16* __restrict__ k_new,
+    const __bf16* __restrict__ v_new, const int32_t* __restrict__ seqlens, PageMap pm, int B, int Hkv, int N) {
+  constexpr int PER_ROW = D / 8;
+  const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gt >= (int64_t)B * Hkv * PER_ROW) return;
+  const int c = (int)(gt % PER_ROW);
+  const int bh = (int)(gt / PER_ROW);
+  const int b = bh / Hkv, hk = bh % Hkv;
+  const int pos = seqlens[b];
+  if (pos < 0 || pos >= N) return;
+  int64_t row;
+  if constexpr (PAGED) {
+    const int page = min(max(pm.table[(int64_t)b * pm.max_pages + (pos >> pm.shift)], 0), pm.num_pages - 1);
+    row = ((int64_t)page << pm.shift) + (pos & ((1 << pm.shift) - 1));
+  } else {
+    row = (int64_t)b * N + pos;
+  }
+  const int64_t dst = (row * Hkv + hk) * D + c * 8;
+  const int64_t src = ((int64_t)b * Hkv + hk) * D + c * 8;
+  *reinterpret_cast<u32x4*>(kc + dst) = *reinterpret_cast<const u32x4*>(k_new + src);
+  *reinterpret_cast<u32x4*>(vc + dst) = *reinterpret_cast<const u32x4*>(v_new + src);
+}
+
+// Chunk rows are at most this many pages long in the paged split kernel
+// (chunks of <= 512 rows, pages of >= 16 rows, plus one partial page).
+constexpr int kDecMaxChunkPages = 64;
+
+template <int D, int GP, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ kc, const __bf16* __restrict__ vc,
     const int32_t* __restrict__ seqlens, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int B, int Hq, int Hkv, int Lmax, int chunk, int nsplit, float scale_log2) {
+    int B, int Hq, int Hkv, int Lmax, int chunk, int nsplit, float scale_log2, int append, PageMap pm) {
   constexpr int LPT = D / 8;
   constexpr int RPW = 64 / LPT;
   constexpr int NSTATE = DecSmem<D, GP>::NSTATE;
   __shared__ float sm_m[NSTATE][GP];
   __shared__ float sm_l[NSTATE][GP];
   __shared__ float sm_o[NSTATE][GP][D];
+  __shared__ int sm_page[PAGED ? kDecMaxChunkPages : 1];
 
   const int HG = Hq / GP;
   const int bid = blockIdx.x;
   const int hg = bid % HG;
   const int s = (bid / HG) % nsplit;
   const int b = bid / (HG * nsplit);
-  const int L = seqlens[b];
+  const int L = seqlens[b] + append;
   if (L < 1 || L > Lmax) return;
   const int start = s * chunk;
   if (start >= L) return;
   const int end = min(L, start + chunk);
+  const int first_page = PAGED ? (start >> pm.shift) : 0;
+  if constexpr (PAGED) {
+    const int n_pages = ((end - 1) >> pm.shift) - first_page + 1;
+    for (int i = threadIdx.x; i < n_pages; i += kDecThreads)
+      sm_page[i] = min(max(pm.table[(int64_t)b * pm.max_pages + first_page + i], 0), pm.num_pages - 1);
+    __syncthreads();
+  }
   const int h0 = hg * GP;                // first query head of this workgroup
   const int hk = h0 / (Hq / Hkv);        // its kv head (GP divides the group size)
 
@@ -75,8 +124,17 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   }
 
   const int64_t row_stride = (int64_t)Hkv * D;
-  const __bf16* kbase = kc + (int64_t)b * Lmax * row_stride + (int64_t)hk * D + dl * 8;
-  const __bf16* vbase = vc + (int64_t)b * Lmax * row_stride + (int64_t)hk * D + dl * 8;
+  const int64_t seq_rows = PAGED ? 0 : (int64_t)b * Lmax;
+  const __bf16* kbase = kc + seq_rows * row_stride + (int64_t)hk * D + dl * 8;
+  const __bf16* vbase = vc + seq_rows * row_stride + (int64_t)hk * D + dl * 8;
+  // Storage row of logical row `row` of this sequence.
+  auto phys = [&](int row) -> int64_t {
+    if constexpr (PAGED) {
+      return ((int64_t)sm_page[(row >> pm.shift) - first_page] << pm.shift) + (row & ((1 << pm.shift) - 1));
+    } else {
+      return row;
+    }
+  };
 
   float m[GP], l[GP], acc[GP][8];
 #pragma unroll
@@ -94,9 +152,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
   auto load = [&](int base) {
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
-      const int row = min(base + u * kDecWaves * RPW + state, end - 1);
-      kr[u] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)row * row_stride);
-      vr[u] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)row * row_stride);
+      const int64_t row = phys(min(base + u * kDecWaves * RPW + state, end - 1));
+      kr[u] = *reinterpret_cast<const u32x4*>(kbase + row * row_stride);
+      vr[u] = *reinterpret_cast<const u32x4*>(vbase + row * row_stride);
     }
   };
 
@@ -174,12 +232,12 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const int32_t* __restrict__ seqlens,
-    __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Lmax, int chunk, int nsplit) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Lmax, int chunk, int nsplit, int append) {
   constexpr int PER = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / Hq;
   const int tid = threadIdx.x;
-  const int L = seqlens[b];
+  const int L = seqlens[b] + append;
   __bf16* orow = o + (int64_t)bh * D;
   if (L < 1 || L > Lmax) {
 #pragma unroll
@@ -210,23 +268,39 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
   if (tid == 0 && lse) lse[bh] = (mm + __log2f(wsum)) * kLn2;
 }
 
-template <int D, int GP>
+PageMap page_map(const DecodeArgs& a) {
+  return PageMap{a.block_table, a.page_shift, a.max_pages, a.num_pages};
+}
+
+template <int D, int GP, bool PAGED>
 hipError_t launch_split(const DecodeArgs& a, int chunk, int nsplit, float* part_o, float* part_lse) {
   const int64_t grid = (int64_t)a.B * nsplit * (a.Hq / GP);
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((decode_split_kernel<D, GP>), dim3((unsigned)grid), dim3(kDecThreads), 0, a.stream,
+  hipLaunchKernelGGL((decode_split_kernel<D, GP, PAGED>), dim3((unsigned)grid), dim3(kDecThreads), 0, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k_cache, (const __bf16*)a.v_cache, a.seqlens,
-                     part_o, part_lse, a.B, a.Hq, a.Hkv, a.N, chunk, nsplit, a.scale * kLog2e);
+                     part_o, part_lse, a.B, a.Hq, a.Hkv, a.N, chunk, nsplit, a.scale * kLog2e,
+                     a.k_new ? 1 : 0, page_map(a));
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_split_gp(const DecodeArgs& a, int gp, int chunk, int nsplit, float* po, float* pl) {
   switch (gp) {
-    case 1: return launch_split<D, 1>(a, chunk, nsplit, po, pl);
-    case 2: return launch_split<D, 2>(a, chunk, nsplit, po, pl);
-    default: return launch_split<D, 4>(a, chunk, nsplit, po, pl);
+    case 1: return launch_split<D, 1, PAGED>(a, chunk, nsplit, po, pl);
+    case 2: return launch_split<D, 2, PAGED>(a, chunk, nsplit, po, pl);
+    default: return launch_split<D, 4, PAGED>(a, chunk, nsplit, po, pl);
   }
+}
+
+template <int D, bool PAGED>
+hipError_t launch_append(const DecodeArgs& a) {
+  const int64_t threads = (int64_t)a.B * a.Hkv * (D / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_append_kernel<D, PAGED>), dim3((unsigned)grid), dim3(256), 0, a.stream,
+                     (__bf16*)a.k_cache, (__bf16*)a.v_cache, (const __bf16*)a.k_new, (const __bf16*)a.v_new,
+                     a.seqlens, page_map(a), a.B, a.Hkv, a.N);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -249,17 +323,30 @@ void decode_split_plan(int N, int num_splits, int* chunk, int* nsplit) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, float* part_o, float* part_lse, int chunk, int nsplit) {
+  const bool paged = a.block_table != nullptr;
+  hipError_t e = hipSuccess;
+  if (a.k_new) {
+    if (a.d == 64) e = paged ? launch_append<64, true>(a) : launch_append<64, false>(a);
+    else e = paged ? launch_append<128, true>(a) : launch_append<128, false>(a);
+    if (e != hipSuccess) return e;
+  }
   const int gp = decode_heads_per_group(a.Hq, a.Hkv);
-  hipError_t e = a.d == 64 ? launch_split_gp<64>(a, gp, chunk, nsplit, part_o, part_lse)
-                           : launch_split_gp<128>(a, gp, chunk, nsplit, part_o, part_lse);
+  if (a.d == 64) {
+    e = paged ? launch_split_gp<64, true>(a, gp, chunk, nsplit, part_o, part_lse)
+              : launch_split_gp<64, false>(a, gp, chunk, nsplit, part_o, part_lse);
+  } else {
+    e = paged ? launch_split_gp<128, true>(a, gp, chunk, nsplit, part_o, part_lse)
+              : launch_split_gp<128, false>(a, gp, chunk, nsplit, part_o, part_lse);
+  }
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)a.B * a.Hq;
+  const int append = a.k_new ? 1 : 0;
   if (a.d == 64) {
     hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)grid), dim3(64), 0, a.stream, part_o, part_lse,
-                       a.seqlens, (__bf16*)a.o, a.lse, a.B, a.Hq, a.N, chunk, nsplit);
+                       a.seqlens, (__bf16*)a.o, a.lse, a.B, a.Hq, a.N, chunk, nsplit, append);
   } else {
     hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)grid), dim3(64), 0, a.stream, part_o, part_lse,
-                       a.seqlens, (__bf16*)a.o, a.lse, a.B, a.Hq, a.N, chunk, nsplit);
+                       a.seqlens, (__bf16*)a.o, a.lse, a.B, a.Hq, a.N, chunk, nsplit, append);
   }
   return hipGetLastError();
 }

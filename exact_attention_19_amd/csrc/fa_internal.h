@@ -67,9 +67,20 @@ struct DecodeArgs {
   const int32_t* seqlens;
   void* o;
   float* lse;
-  int B, Hq, Hkv, N, d;
+  int B, Hq, Hkv, N, d;  // N: rows each sequence can hold (paged: max_pages << page_shift)
   float scale;
   hipStream_t stream;
+  // Paged cache: k_cache/v_cache are [num_pages, 1 << page_shift, Hkv, d] and
+  // block_table [B, max_pages] maps logical page p of sequence b to a page
+  // (ids are clamped to [0, num_pages)). NULL block_table: [B, N, Hkv, d].
+  const int32_t* block_table = nullptr;
+  int page_shift = 0;
+  int max_pages = 0;
+  int num_pages = 0;
+  // Append: one new K/V row per sequence ([B, Hkv, d]) written at row
+  // seqlens[b] before attention, which then covers seqlens[b] + 1 rows.
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
 };
 
 // Decode splits the cache into chunks of this many rows unless told otherwise.

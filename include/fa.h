@@ -198,6 +198,42 @@ fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_ca
                             int B, int Hq, int Hkv, int N, int d, float scale, int causal,
                             int num_splits, int dtype, void* stream);
 
+/*
+ * Decode with an in-place cache append and/or a paged KV cache
+ * (flash_attn_with_kvcache updates k_cache/v_cache in place: hysenlabs
+ * digest, outputs section; paged KV cache: v2.5 entry of the changelog in
+ * the constraints section). One query per sequence as fa_decode_kvcache.
+ *   block_table == NULL: contiguous cache k_cache, v_cache [B, cache_rows, Hkv, d];
+ *     each sequence holds N = cache_rows rows.
+ *   block_table != NULL: paged cache k_cache, v_cache [num_pages, page_size, Hkv, d]
+ *     (page_size a power of two >= 16) and block_table: device int32
+ *     [B, max_pages_per_seq]; logical row t of sequence b is row
+ *     t % page_size of page block_table[b][t / page_size]. Each sequence
+ *     holds N = max_pages_per_seq * page_size rows; cache_rows is ignored.
+ *     Page ids are clamped to [0, num_pages) on the device, so a bad table
+ *     cannot cause accesses outside the pool (results are then unspecified).
+ *   k_new, v_new (both NULL or both given): device bf16 [B, Hkv, d], one new
+ *     token per sequence, written in place at logical row cache_seqlens[b]
+ *     before attention; attention then covers cache_seqlens[b] + 1 rows.
+ *     cache_seqlens itself is not modified. A position outside [0, N) is not
+ *     written.
+ * Attention covers L_b = cache_seqlens[b] (+ 1 with an append) rows; an L_b
+ * outside [1, N] gives O = 0 and LSE = -inf for that sequence.
+ * Workspace: fa_decode_workspace_bytes(B, Hq, Hkv, N, d, num_splits) with the
+ *   N above. With a paged cache num_splits must be 0 (automatic) or at least
+ *   ceil(N / 512) (chunks of at most 512 rows).
+ * Errors: as fa_decode_kvcache, plus FA_ERR_INVALID_ARG for a bad page_size,
+ *   max_pages_per_seq or num_pages <= 0 (paged), only one of k_new/v_new,
+ *   misaligned block_table/k_new/v_new, or too few splits for a paged cache.
+ */
+fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache,
+                                const int32_t* cache_seqlens, const int32_t* block_table,
+                                int max_pages_per_seq, int num_pages, int page_size,
+                                const void* k_new, const void* v_new, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                                int cache_rows, int d, float scale, int causal, int num_splits,
+                                int dtype, void* stream);
+
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

@@ -134,6 +134,26 @@ def test_varlen_validation(lib):
         assert lib.fa_last_error().decode().startswith("fa_fwd_varlen")
 
 
+def test_decode_ext_validation(lib):
+    # q kc vc seqlens table, max_pages, num_pages, page_size, k_new, v_new, o, lse, ws, ws_bytes,
+    # B, Hq, Hkv, cache_rows, d, scale, causal, num_splits, dtype, stream
+    ws = lib.fa_decode_workspace_bytes(2, 8, 2, 64 * 16, 128, 0)
+    args = [FAKE] * 5 + [16, 40, 64, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 2, 8, 2, 0, 128, 0.1, 0, 0,
+                         _lib.FA_BF16, None]
+    for idx, val, status in ((7, 48, _lib.FA_ERR_INVALID_ARG),      # page_size not a power of two
+                             (7, 8, _lib.FA_ERR_INVALID_ARG),       # page_size < 16
+                             (5, 0, _lib.FA_ERR_INVALID_ARG),       # max_pages_per_seq
+                             (6, 0, _lib.FA_ERR_INVALID_ARG),       # num_pages
+                             (9, None, _lib.FA_ERR_INVALID_ARG),    # v_new without k_new
+                             (21, 1, _lib.FA_ERR_INVALID_ARG),      # too few splits for pages
+                             (13, ws - 4, _lib.FA_ERR_WORKSPACE),
+                             (22, _lib.FA_FP32, _lib.FA_ERR_UNSUPPORTED)):
+        bad = list(args)
+        bad[idx] = val
+        assert lib.fa_decode_kvcache_ext(*bad) == status, (idx, val)
+        assert lib.fa_last_error().decode().startswith("fa_decode_kvcache_ext")
+
+
 def test_decode_validation(lib):
     ws = lib.fa_decode_workspace_bytes(2, 8, 2, 1000, 128, 0)
     args = [FAKE] * 7 + [ws, 2, 8, 2, 1000, 128, 0.1, 0, 0, _lib.FA_BF16, None]
