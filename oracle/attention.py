@@ -59,8 +59,15 @@ What is computed, and where the pages define it:
   bottom-right causal alignment inside each sequence. This packing is a
   stated reading (the pages only name the functions).
 
-A fully masked row (possible when causal and Nq > Nk, or with a window that
-leaves a row no keys) has O = 0 and LSE = -inf by convention.
+* Block-sparse attention (abeam summary, "Block-sparse への拡張"): blocks of
+  the score matrix known to be zero are left out and FlashAttention runs on
+  the rest. Reading taken: a 0/1 block mask over ``block`` x ``block`` tiles
+  of (query, key) positions; positions in a 0 block are excluded exactly
+  like masked ones (score -inf), on top of any causal mask.
+
+A fully masked row (possible when causal and Nq > Nk, with a window that
+leaves a row no keys, or with a block mask) has O = 0 and LSE = -inf by
+convention.
 
 Inputs are numpy arrays of any float dtype; they are converted exactly to
 float64. Layouts: q, o, do, dq ``[B, Nq, Hq, d]``; k, v, dk, dv
@@ -77,7 +84,8 @@ def _check_heads(hq: int, hkv: int) -> int:
     return hq // hkv
 
 
-def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=None, nq=None, window=(-1, -1)):
+def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=None, nq=None, window=(-1, -1),
+               keep_extra=None):
     """Scores, probabilities and logsumexp for one (batch, head).
 
     q: [R, d] query rows, k: [Nk, d] (float64). ``rows`` gives the absolute
@@ -102,6 +110,8 @@ def head_probs(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, rows=No
         s = np.where(j >= diag - wl, s, -np.inf)
     if wr >= 0:
         s = np.where(j <= diag + wr, s, -np.inf)
+    if keep_extra is not None:               # [R, Nk] booleans (block-sparse pattern)
+        s = np.where(keep_extra, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     empty = ~np.isfinite(m)
     m_safe = np.where(empty, 0.0, m)
@@ -228,6 +238,38 @@ def attn_fwd_varlen(q, k, v, cu_q, cu_k, scale: float, causal: bool, window=(-1,
         ob, lb = attn_fwd(q[None, q0:q1], k[None, k0:k1], v[None, k0:k1], scale, causal, window)
         o[q0:q1] = ob[0]
         lse[:, q0:q1] = lb[0]
+    return o, lse
+
+
+def block_keep(block_mask, block: int, nq: int, nk: int):
+    """Expand a [ceil(nq/block), ceil(nk/block)] 0/1 block mask to [nq, nk]."""
+    bm = np.asarray(block_mask).astype(bool)
+    return bm[np.arange(nq)[:, None] // block, np.arange(nk)[None, :] // block]
+
+
+def attn_fwd_blocksparse(q, k, v, block_mask, block: int, scale: float, causal: bool):
+    """Forward restricted to the 1-blocks of ``block_mask``.
+
+    q: [B, N, Hq, d]; k, v: [B, N, Hkv, d]; block_mask: [nbq, nbk] shared by
+    every (batch, head), or [B, Hq, nbq, nbk]. Returns (o, lse) as attn_fwd.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, nq, hq, d = q.shape
+    nk, hkv = k.shape[1], k.shape[2]
+    g = _check_heads(hq, hkv)
+    bm = np.asarray(block_mask)
+    o = np.zeros((b_, nq, hq, d))
+    lse = np.zeros((b_, hq, nq))
+    for b in range(b_):
+        for h in range(hq):
+            kh = h // g
+            mask_bh = bm if bm.ndim == 2 else bm[b, h]
+            _, p, lse_bh = head_probs(q[b, :, h, :], k[b, :, kh, :], scale, causal,
+                                      keep_extra=block_keep(mask_bh, block, nq, nk))
+            o[b, :, h, :] = p @ v[b, :, kh, :]
+            lse[b, h, :] = lse_bh
     return o, lse
 
 

@@ -459,8 +459,56 @@ def pin_paged_decode_properties(m):
     np.testing.assert_array_equal(kp3[inv].reshape(B, mp * ps, Hkv, d), kc4)
 
 
+def pin_golden_blocksparse(m):
+    data = json.load(open(GOLDEN))
+    for case in data["blocksparse"]:
+        q, k, v = _arr(case["q"]), _arr(case["k"]), _arr(case["v"])
+        o, lse = m.attn_fwd_blocksparse(q, k, v, np.array(case["block_mask"]), case["block"], _expr(case["scale"]),
+                                        case["causal"])
+        np.testing.assert_allclose(o, _arr(case["o"]), rtol=0, atol=1e-13, err_msg=case["name"])
+        want = _arr(case["lse"])
+        np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(want))
+        fin = np.isfinite(want)
+        np.testing.assert_allclose(lse[fin], want[fin], rtol=0, atol=1e-13, err_msg=case["name"])
+
+
+def pin_blocksparse_properties(m):
+    """All-ones mask is dense attention; a block-diagonal mask is independent
+    attention inside each block; a random mask equals scalar brute force with
+    the block condition written out."""
+    rng = np.random.default_rng(25)
+    q, k, v = _rand(rng, 2, 10, 4, 3), _rand(rng, 2, 10, 2, 3), _rand(rng, 2, 10, 2, 3)
+    for causal in (False, True):
+        od, ld = m.attn_fwd(q, k, v, 0.8, causal)
+        o1, l1 = m.attn_fwd_blocksparse(q, k, v, np.ones((4, 4)), 3, 0.8, causal)
+        np.testing.assert_allclose(o1, od, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l1, ld, rtol=0, atol=1e-14)
+    ob, lb = m.attn_fwd_blocksparse(q, k, v, np.eye(4), 3, 0.8, False)
+    for blk in range(4):
+        sl = slice(3 * blk, min(3 * blk + 3, 10))
+        oe, le = m.attn_fwd(q[:, sl], k[:, sl], v[:, sl], 0.8, False)
+        np.testing.assert_allclose(ob[:, sl], oe, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lb[:, :, sl], le, rtol=0, atol=1e-14)
+    mask = rng.integers(0, 2, (2, 4, 4, 4))
+    for causal in (False, True):
+        o, lse = m.attn_fwd_blocksparse(q, k, v, mask, 3, 0.8, causal)
+        for b in range(2):
+            for h in range(4):
+                for i in range(10):
+                    sc = [(j, 0.8 * float(np.dot(q[b, i, h], k[b, j, h // 2]))) for j in range(10)
+                          if mask[b, h, i // 3, j // 3] and not (causal and j > i)]
+                    if not sc:
+                        assert np.isneginf(lse[b, h, i]) and not o[b, i, h].any()
+                        continue
+                    tot = sum(math.exp(x) for _, x in sc)
+                    want = sum(math.exp(x) / tot * v[b, j, h // 2] for j, x in sc)
+                    np.testing.assert_allclose(o[b, i, h], want, rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(lse[b, h, i], math.log(tot), rtol=0, atol=1e-12)
+
+
 PINS += [pin_golden_window, pin_golden_varlen, pin_window_brute_force, pin_window_special_cases,
-         pin_varlen_is_per_sequence_dense, pin_golden_decode_paged, pin_paged_decode_properties]
+         pin_varlen_is_per_sequence_dense, pin_golden_decode_paged, pin_paged_decode_properties,
+         pin_golden_blocksparse, pin_blocksparse_properties]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -508,6 +556,11 @@ MUTANTS = {
                               "return pages[np.asarray(block_table)[b, t // page_size], (t + 1) % page_size]"),
     "paged_append_before_last_row": ("            t = int(lens[b])\n", "            t = int(lens[b]) - 1\n"),
     "paged_append_not_attended": ("        lens = lens + 1\n", "        lens = lens + 0\n"),
+    "blocksparse_mask_transposed": ("return bm[np.arange(nq)[:, None] // block, np.arange(nk)[None, :] // block]",
+                                    "return bm.T[np.arange(nq)[:, None] // block, np.arange(nk)[None, :] // block]"),
+    "blocksparse_block_off_by_one": ("bm[np.arange(nq)[:, None] // block, np.arange(nk)[None, :] // block]",
+                                     "bm[np.arange(nq)[:, None] // block, np.minimum(np.arange(nk)[None, :] + 1, nk - 1) // block]"),
+    "blocksparse_mask_ignored": ("        s = np.where(keep_extra, s, -np.inf)", "        s = s"),
     "varlen_lse_row_major": ("lse[:, q0:q1] = lb[0]", "lse[:, q0:q1] = lb[0][::-1] if lb.shape[1] > 1 else lb[0]"),
 }
 
