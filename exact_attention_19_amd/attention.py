@@ -116,6 +116,33 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
     return out, lse
 
 
+def fa_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False):
+    """Block-sparse forward (bf16, d = 128): block_mask is a uint8 device tensor
+    of [nb, nb] (shared) or [B, Hq, nb, nb] bytes, nb = ceil(N / 128).
+    Returns (o, lse) laid out as fa_fwd."""
+    _check_tensor("q", q, torch.bfloat16, 4)
+    dev = q.device
+    _check_tensor("k", k, torch.bfloat16, 4, dev)
+    _check_tensor("v", v, torch.bfloat16, 4, dev)
+    _check_tensor("block_mask", block_mask, torch.uint8, None, dev)
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nb = (N + 127) // 128
+    if block_mask.dim() == 2 and tuple(block_mask.shape) == (nb, nb):
+        stride = 0
+    elif block_mask.dim() == 4 and tuple(block_mask.shape) == (B, Hq, nb, nb):
+        stride = nb * nb
+    else:
+        raise ValueError(f"block_mask must be [{nb}, {nb}] or [{B}, {Hq}, {nb}, {nb}]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+    st = _lib.load().fa_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(block_mask), stride,
+                                        B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16, _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
 def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1)):
     """Attention backward from the forward's O and LSE. Returns (dq, dk, dv).
     A window other than (-1, -1) calls fa_bwd_window (d = 128)."""

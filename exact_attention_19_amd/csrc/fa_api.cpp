@@ -194,6 +194,33 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   return hip_status(fn, fa::launch_fwd_seq(a, seq));
 }
 
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const uint8_t* block_mask, long long mask_head_stride, int B, int Hq, int Hkv, int N,
+                             int d, float scale, int causal, int dtype, void* stream) {
+  static const char* fn = "fa_fwd_blocksparse";
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is supported", fn);
+  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: d = 128 only (got %d)", fn, d);
+  const int nb = (N + fa::kBlockSparseBlock - 1) / fa::kBlockSparseBlock;
+  if (nb > fa::kBlockSparseMaxBlocks)
+    return fail(FA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, fa::kBlockSparseMaxBlocks * fa::kBlockSparseBlock);
+  if (mask_head_stride != 0 && mask_head_stride < (long long)nb * nb)
+    return fail(FA_ERR_INVALID_ARG, "%s: mask_head_stride %lld is neither 0 nor >= %d", fn, mask_head_stride, nb * nb);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k", k, 16));
+  FA_TRY(check_ptr(fn, "v", v, 16));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  FA_TRY(check_ptr(fn, "lse", lse, 4));
+  FA_TRY(check_ptr(fn, "block_mask", block_mask, 1));
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal ? 1 : 0, dtype,
+                reinterpret_cast<hipStream_t>(stream)};
+  fa::FwdSeq seq;
+  seq.block_mask = block_mask;
+  seq.mask_stride = mask_head_stride;
+  seq.nbk = nb;
+  return hip_status(fn, fa::launch_fwd_blocksparse(a, seq));
+}
+
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
   (void)Hkv;
   (void)d;

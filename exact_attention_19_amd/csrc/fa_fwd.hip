@@ -293,6 +293,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     int num_q_tiles, FwdSeq seq) {
   constexpr bool VARLEN = (MODE & kModeVarlen) != 0;
   constexpr bool WINDOW = (MODE & kModeWindow) != 0;
+  constexpr bool BSPARSE = (MODE & kModeBlockSparse) != 0;
   constexpr int D = 128;
   constexpr int WQ = 32 * QB;           // query rows per wave
   constexpr int BM = NWAVES * WQ;       // query rows per workgroup
@@ -301,6 +302,8 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   constexpr int TILE = 64 * 256;        // bytes of one 64 x 128 bf16 tile
   constexpr int STAGE = 2 * TILE;       // K tile then V tile
   constexpr int CPW = 16 / NWAVES;      // 1 KB chunks per wave per tile
+  static_assert(!BSPARSE || (BM == kBlockSparseBlock && !VARLEN && !WINDOW),
+                "block-sparse mode: one 128-row query block per workgroup, dense batch");
   extern __shared__ __align__(1024) unsigned char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   // allocator keep them in VGPRs instead (and spill), so the rare rescale goes
   // through a 4 KB per-wave LDS slot: store, scale in VGPRs, store, load
   // back, with compiler barriers so the round trip stays.
-  float* resc_slot = reinterpret_cast<float*>(smem + NSTAGE * STAGE + wave * 4096) + lane * 16;
+  float* resc_slot = reinterpret_cast<float*>(smem + NSTAGE * STAGE + wave * 4096) + lane * 16;  // QB > 1 only
   auto rescale_o = [&](int j, float alpha) __attribute__((always_inline)) {
     if constexpr (QB == 1) {
 #pragma unroll
@@ -636,6 +639,74 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   f_end = max(min(f_end, t_end), f_begin);
   f_begin = min(f_begin, t_end);
 
+  if constexpr (BSPARSE) {
+    // Active key tiles of this query block, in order: wave 0 scans the mask
+    // row 64 blocks at a time (ballot + prefix count) and writes the two
+    // 64-key tiles of every active block to an LDS list; tiles at or past
+    // t_end (beyond the causal diagonal or N) are dropped.
+    constexpr int LIST_OFF = NSTAGE * STAGE;
+    unsigned short* list = reinterpret_cast<unsigned short*>(smem + LIST_OFF);
+    int* count_slot = reinterpret_cast<int*>(smem + LIST_OFF + 2 * 2 * kBlockSparseMaxBlocks);
+    if (wave == 0) {
+      const uint8_t* mrow = seq.block_mask + ((int64_t)b * Hq + hq) * seq.mask_stride + (int64_t)qt * seq.nbk;
+      const int blk_hi = min(seq.nbk, (t_end + 1) / 2);
+      int cnt = 0;
+      for (int c0 = 0; c0 < blk_hi; c0 += 64) {
+        const int blk = c0 + lane;
+        const bool act = blk < blk_hi && mrow[blk] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(act);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+        if (act) {
+          list[cnt + 2 * below] = (unsigned short)(2 * blk);
+          list[cnt + 2 * below + 1] = (unsigned short)(2 * blk + 1);
+        }
+        cnt += 2 * __builtin_popcountll(bal);
+      }
+      // Only the last block's second tile can lie past the end (its first
+      // tile 2*blk <= t_end - 1 since blk < (t_end + 1) / 2). The list was
+      // written by this wave, so its LDS writes are visible to this read.
+      if (cnt > 0 && (int)list[cnt - 1] >= t_end) --cnt;
+      if (lane == 0) *count_slot = cnt;
+    }
+    __syncthreads();
+    const int n_act = uniform(*count_slot);
+    auto tile_at = [&](int i) __attribute__((always_inline)) { return uniform((int)list[i]); };
+    auto bs_step = [&](int i, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
+      constexpr int STG = decltype(stage_tag)::value;
+      const bool more = i + NSTAGE - 1 < n_act;
+      if (more) issue(tile_at(i + NSTAGE - 1), (STG + NSTAGE - 1) % NSTAGE);
+      const int tt = tile_at(i);
+      const int k0 = tt * 64;
+      const bool skip = !wave_active || (CAUSAL && k0 > qw0 + WQ - 1 + off);
+      if (!skip) {
+        const unsigned char* ks = smem + STG * STAGE;
+        tile(ks, ks + TILE, k0, mask_tag);
+      }
+      if (more) wait_vmcnt<(NSTAGE - 2) * DMA_PER_STEP>();
+      else wait_vmcnt<0>();
+      barrier_keep_dma();
+    };
+    auto bs_any = [&](int i) __attribute__((always_inline)) {
+      const int tt = tile_at(i);
+      const bool full = tt < f_end;
+      const int stg = i % NSTAGE;
+      if (stg == 0) {
+        if (full) bs_step(i, std::integral_constant<int, 0>{}, std::false_type{});
+        else bs_step(i, std::integral_constant<int, 0>{}, std::true_type{});
+      } else {
+        if (full) bs_step(i, std::integral_constant<int, 1 % NSTAGE>{}, std::false_type{});
+        else bs_step(i, std::integral_constant<int, 1 % NSTAGE>{}, std::true_type{});
+      }
+    };
+    static_assert(NSTAGE == 2, "block-sparse list walk uses two stages");
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i) {
+      if (i < n_act) issue(tile_at(i), i);
+    }
+    wait_vmcnt<0>();
+    barrier_keep_dma();
+    for (int i = 0; i < n_act; ++i) bs_any(i);
+  } else {
 #pragma unroll
   for (int i = 0; i < NSTAGE - 1; ++i) {
     if (t_begin + i < t_end) issue(t_begin + i, i);
@@ -652,6 +723,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   }
   for (; t < f_end; ++t) step_any(t, std::false_type{});
   for (; t < t_end; ++t) step_any(t, std::true_type{});
+  }
 
   if (!wave_active) return;
   const int64_t lse_base = VARLEN ? (int64_t)hq * seq.total_q + q_start : ((int64_t)b * Hq + hq) * N;
@@ -770,7 +842,10 @@ hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   const int num_q_tiles = (rows + BM - 1) / BM;
   const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + NWAVES * 4096;  // tile ring + rescale slots
+  // Tile ring, then (QB > 1) one 4 KB rescale slot per wave or (block-sparse)
+  // the active-tile list and its count.
+  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + (QB > 1 ? NWAVES * 4096 : 0) +
+                          ((MODE & kModeBlockSparse) ? 2 * 2 * kBlockSparseMaxBlocks + 16 : 0);
   auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -802,6 +877,11 @@ hipError_t launch_fwd(const FwdArgs& a) {
     return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
   }
   return a.causal ? launch_d128<4, 2, 1, true>(a) : launch_d128<4, 2, 1, false>(a);
+}
+
+hipError_t launch_fwd_blocksparse(const FwdArgs& a, const FwdSeq& seq) {
+  return a.causal ? launch_d128<4, 2, 1, true, kModeBlockSparse>(a, seq)
+                  : launch_d128<4, 2, 1, false, kModeBlockSparse>(a, seq);
 }
 
 hipError_t launch_fwd_seq(const FwdArgs& a, const FwdSeq& seq) {

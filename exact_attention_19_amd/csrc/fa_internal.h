@@ -37,10 +37,19 @@ struct FwdSeq {
   int max_q = 0;
   int win_left = -1;
   int win_right = -1;
+  // Block-sparse: 0/1 bytes over kBlockSparseBlock x kBlockSparseBlock tiles,
+  // [ceil(N/128)] x [nbk] per (b, hq) at block_mask + (b*Hq + hq)*mask_stride
+  // (stride 0: one mask shared by all).
+  const uint8_t* block_mask = nullptr;
+  int64_t mask_stride = 0;
+  int nbk = 0;
 };
 
 constexpr int kModeVarlen = 1;
 constexpr int kModeWindow = 2;
+constexpr int kModeBlockSparse = 4;
+constexpr int kBlockSparseBlock = 128;
+constexpr int kBlockSparseMaxBlocks = 2048;  // N <= 262144
 
 struct BwdArgs {
   const void* q;
@@ -92,6 +101,8 @@ hipError_t launch_fwd(const FwdArgs& a);
 // Varlen and/or windowed forward (bf16, d = 128). a.N is ignored; a.B is
 // the number of sequences.
 hipError_t launch_fwd_seq(const FwdArgs& a, const FwdSeq& seq);
+// Block-sparse forward (bf16, d = 128, dense batch).
+hipError_t launch_fwd_blocksparse(const FwdArgs& a, const FwdSeq& seq);
 
 // Backward workspace: D = rowsum(dO * O) at `delta` ([B, Hq, N] float32),
 // then LSE * log2(e) at delta + bwd_vec_stride(...) (same shape).

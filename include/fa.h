@@ -119,6 +119,25 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
                         int Hq, int Hkv, int d, float scale, int causal,
                         int window_left, int window_right, int dtype, void* stream);
 
+/*
+ * Block-sparse forward (the block-sparse FlashAttention of the abeam.tech
+ * summary, "Block-sparse への拡張": blocks known to be zero are skipped and the
+ * rest is computed as usual). block_mask holds one byte per 128 x 128 block of
+ * (query, key) positions, nb = ceil(N / 128) rows of nb bytes, row-major;
+ * (b, hq) uses block_mask + (b * Hq + hq) * mask_head_stride (stride 0: one
+ * mask for every batch entry and head). Positions in a zero block are excluded
+ * like masked ones; causal = 1 applies the causal mask as well. A row that
+ * keeps no key has O = 0, LSE = -inf. Skipped blocks cost neither loads nor
+ * arithmetic. Layouts, alignment and outputs as fa_fwd.
+ * Errors: as fa_fwd, plus FA_ERR_UNSUPPORTED for d != 128, dtype != FA_BF16 or
+ * N > 262144; FA_ERR_INVALID_ARG for a NULL mask or a stride that is neither 0
+ * nor >= nb * nb.
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const uint8_t* block_mask, long long mask_head_stride,
+                             int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                             int dtype, void* stream);
+
 /* Bytes of device workspace fa_bwd needs for these sizes (256-byte aligned). */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
 

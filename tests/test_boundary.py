@@ -115,6 +115,19 @@ def test_bwd_window_validation(lib):
     assert lib.fa_last_error().decode().startswith("fa_bwd_window")
 
 
+def test_blocksparse_validation(lib):
+    args = [FAKE] * 6 + [0, 1, 4, 2, 1000, 128, 0.1, 1, _lib.FA_BF16, None]
+    for idx, val, status in ((5, None, _lib.FA_ERR_INVALID_ARG),      # block_mask
+                             (6, 3, _lib.FA_ERR_INVALID_ARG),         # stride below nb*nb
+                             (11, 64, _lib.FA_ERR_UNSUPPORTED),       # d
+                             (10, 300000, _lib.FA_ERR_UNSUPPORTED),   # N too large
+                             (14, _lib.FA_FP32, _lib.FA_ERR_UNSUPPORTED)):
+        bad = list(args)
+        bad[idx] = val
+        assert lib.fa_fwd_blocksparse(*bad) == status, (idx, val)
+        assert lib.fa_last_error().decode().startswith("fa_fwd_blocksparse")
+
+
 def test_varlen_validation(lib):
     # q k v o lse cu_q cu_k, B, max_q, total_q, total_k, Hq, Hkv, d, scale, causal, wl, wr, dtype, stream
     args = [FAKE] * 7 + [3, 100, 200, 150, 4, 2, 128, 0.1, 1, -1, -1, _lib.FA_BF16, None]
