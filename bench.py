@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle sample")
     ap.add_argument("--no-decode", action="store_true", help="leave the decode stage out (profiling only)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the secondary measurements (window, varlen, paged decode, block-sparse)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -140,6 +142,113 @@ def cpu_baseline(inp, w, heads: int):
         "sample": f"{heads} of {w.B * w.Hq} heads (b=0, h<{heads}) at full N={w.N}: fp64 forward + backward "
                   f"with S materialised; {dt:.1f} s wall",
     }
+
+
+def _time_ms(fn, reps=5, warm=2):
+    """Mean time of fn() over reps launches, HIP events on the current stream."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _pairs_band(nq, nk, causal, wl=-1, wr=-1):
+    """Visible (query, key) pairs of one head: keys j with i + off - wl <= j <=
+    i + off + wr (and j <= i + off when causal), off = nk - nq."""
+    import numpy as np
+
+    i = np.arange(nq, dtype=np.int64)
+    diag = i + (nk - nq)
+    hi = np.full(nq, nk - 1, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, diag)
+    if wr >= 0:
+        hi = np.minimum(hi, diag + wr)
+    lo = np.zeros(nq, dtype=np.int64) if wl < 0 else np.maximum(diag - wl, 0)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def extras(fa_mod, lib, dev):
+    """Secondary lines: the sliding-window, varlen, paged-decode and
+    block-sparse paths on workloads of the pages' shapes. Each rate uses the
+    algorithmic work (4*d FLOP per visible query-key pair in a forward,
+    2.5x that in a backward; bytes read once for decode)."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    out = {}
+    # Sliding window at the GB200 timing shape, window of 4096 keys (causal).
+    B, N, H, d = 1, 8192, 96, 128
+    wl = 4095
+    inp = workloads.prefill_inputs(B, N, H, H, d, "bf16", seed=1, with_do=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    del inp
+    o, lse = fa_mod.fa_fwd_window(q, k, v, (wl, 0), causal=True)
+    pairs = _pairs_band(N, N, True, wl, 0) * B * H
+    ms_f = _time_ms(lambda: fa_mod.fa_fwd_window(q, k, v, (wl, 0), causal=True))
+    ms_b = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True, window=(wl, 0)))
+    out["window_fwd"] = {"workload": f"B={B} N={N} H={H} d={d} causal window (4095, 0)", "ms": round(ms_f, 4),
+                         "TFLOP/s": round(4 * d * pairs / (ms_f * 1e9), 1)}
+    out["window_bwd"] = {"workload": out["window_fwd"]["workload"], "ms": round(ms_b, 4),
+                         "TFLOP/s": round(2.5 * 4 * d * pairs / (ms_b * 1e9), 1),
+                         "note": "fa_bwd_window: preprocess + dK/dV + dQ kernels"}
+    # Block-sparse at the same shape: a band of 5 blocks plus the first block column.
+    nb = N // 128
+    ib = np.arange(nb)
+    bm = ((np.abs(ib[:, None] - ib[None, :]) <= 2) | (ib[None, :] == 0)).astype(np.uint8)
+    keep = np.kron(bm, np.ones((128, 128), dtype=np.uint8)).astype(bool) & np.tri(N, dtype=bool)
+    pairs = int(keep.sum()) * B * H
+    del keep
+    bmd = torch.from_numpy(bm).to(dev)
+    ms = _time_ms(lambda: fa_mod.fa_fwd_blocksparse(q, k, v, bmd, causal=True))
+    out["blocksparse_fwd"] = {"workload": f"B={B} N={N} H={H} d={d} causal, 128x128 blocks: band |i-j|<=2 "
+                                          f"plus block column 0 ({bm.mean() * 100:.1f}% of blocks)",
+                              "ms": round(ms, 4), "TFLOP/s": round(4 * d * pairs / (ms * 1e9), 1)}
+    del q, k, v, do, o, lse
+    # Varlen prefill: hidden 2048 (16 heads x 128), sequences U[256, 4096] packed to >= 16k tokens.
+    rng = np.random.default_rng(2)
+    lens = []
+    while sum(lens) < 16384:
+        lens.append(int(rng.integers(256, 4097)))
+    vin = workloads.varlen_inputs(lens, lens, 16, 16, d, seed=3)
+    vq, vk, vv = (vin[n].to(dev) for n in ("q", "k", "v"))
+    cq, ck = vin["cu_q"].to(dev), vin["cu_k"].to(dev)
+    pairs = sum(_pairs_band(n, n, True) for n in lens) * 16
+    ms = _time_ms(lambda: fa_mod.fa_fwd_varlen(vq, vk, vv, cq, ck, max(lens), causal=True))
+    out["varlen_fwd"] = {"workload": f"{len(lens)} sequences (U[256,4096], {sum(lens)} tokens) H=16 d=128 causal",
+                         "ms": round(ms, 4), "TFLOP/s": round(4 * d * pairs / (ms * 1e9), 1)}
+    del vq, vk, vv
+    # Paged decode with append: the decode workload in 256-row pages.
+    wd = workloads.WORKLOADS["c5"]
+    seq = workloads.decode_seqlens(wd.B, wd.seq_lo, wd.seq_hi, seed=0)
+    seq = torch.clamp(seq, max=wd.N - 1)                # room for the appended token
+    ps, mp = 256, wd.N // 256
+    kp = torch.randn((wd.B * mp, ps, wd.Hkv, wd.d), device=dev, dtype=torch.bfloat16)
+    vp = torch.randn_like(kp)
+    perm = torch.randperm(wd.B * mp, generator=torch.Generator().manual_seed(4))
+    table = perm.view(wd.B, mp).to(torch.int32).to(dev)
+    qd = workloads.decode_query(wd.B, wd.Hq, wd.d, seed=0).to(dev)
+    kn = torch.randn((wd.B, wd.Hkv, wd.d), device=dev, dtype=torch.bfloat16)
+    sl = seq.to(dev)
+    ms = _time_ms(lambda: fa_mod.fa_decode_kvcache_ext(qd, kp, vp, sl, block_table=table, k_new=kn, v_new=kn))
+    nbytes = 2 * 2 * wd.d * wd.Hkv * int((seq + 1).sum()) + 2 * wd.B * wd.Hq * wd.d * 2 + 4 * wd.B * wd.Hq
+    out["paged_decode_append"] = {"workload": "64 seqs x 1 query, Hq=32 Hkv=8 d=128, L~U[1024,32768]+1, "
+                                              "256-row pages in a shuffled pool, in-place append",
+                                  "ms": round(ms, 4), "GB/s": round(nbytes / (ms * 1e6), 1),
+                                  "note": "append + split + merge kernels; bytes = cache rows read once + q/o/lse"}
+    del kp, vp
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -281,6 +390,14 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, w, args.cpu_heads)
 
+    extra = None
+    if not args.no_extras:
+        if run_decode:
+            del kc, vc
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+        extra = extras(fa, lib, dev)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -307,6 +424,7 @@ def main():
                     "ms": kernels["decode"]["ms"], "sum_cache_len": int(lens.sum())} if run_decode else None),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "extras": extra,
         "wall_s_timed_region": round(wall, 3),
         "gpu": torch.cuda.get_device_name(0),
     }
