@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kDecUnroll = 4;  // cache rows per row group per iteration
+constexpr int kDecUnroll = 8;  // cache rows per row group per iteration
 
 template <int D, int GP>
 struct DecSmem {
@@ -74,8 +74,10 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
 }
 
 // Chunk rows are at most this many pages long in the paged split kernel
-// (chunks of <= 512 rows, pages of >= 16 rows, plus one partial page).
-constexpr int kDecMaxChunkPages = 64;
+// (chunks of <= kDecodeDefaultChunk = 1024 rows, pages of >= 16 rows, plus
+// one partial page).
+constexpr int kDecMaxChunkPages = 128;
+static_assert(kDecodeDefaultChunk / 16 + 1 <= kDecMaxChunkPages, "page list too small");
 
 template <int D, int GP, bool PAGED>
 __global__ __launch_bounds__(kDecThreads) void decode_split_kernel(

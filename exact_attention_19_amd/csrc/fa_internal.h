@@ -93,7 +93,7 @@ struct DecodeArgs {
 };
 
 // Decode splits the cache into chunks of this many rows unless told otherwise.
-constexpr int kDecodeDefaultChunk = 512;
+constexpr int kDecodeDefaultChunk = 1024;
 // Query heads that one decode workgroup serves from a single read of K/V.
 constexpr int kDecodeMaxHeadsPerGroup = 4;
 

@@ -240,7 +240,7 @@ fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_ca
  * outside [1, N] gives O = 0 and LSE = -inf for that sequence.
  * Workspace: fa_decode_workspace_bytes(B, Hq, Hkv, N, d, num_splits) with the
  *   N above. With a paged cache num_splits must be 0 (automatic) or at least
- *   ceil(N / 512) (chunks of at most 512 rows).
+ *   ceil(N / 1024) (chunks of at most 1024 rows).
  * Errors: as fa_decode_kvcache, plus FA_ERR_INVALID_ARG for a bad page_size,
  *   max_pages_per_seq or num_pages <= 0 (paged), only one of k_new/v_new,
  *   misaligned block_table/k_new/v_new, or too few splits for a paged cache.

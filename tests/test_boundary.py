@@ -150,8 +150,9 @@ def test_varlen_validation(lib):
 def test_decode_ext_validation(lib):
     # q kc vc seqlens table, max_pages, num_pages, page_size, k_new, v_new, o, lse, ws, ws_bytes,
     # B, Hq, Hkv, cache_rows, d, scale, causal, num_splits, dtype, stream
-    ws = lib.fa_decode_workspace_bytes(2, 8, 2, 64 * 16, 128, 0)
-    args = [FAKE] * 5 + [16, 40, 64, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 2, 8, 2, 0, 128, 0.1, 0, 0,
+    # 40 pages of 64 rows: 2560 rows per sequence, so one split (a 2560-row chunk) is too few
+    ws = lib.fa_decode_workspace_bytes(2, 8, 2, 64 * 40, 128, 0)
+    args = [FAKE] * 5 + [40, 40, 64, FAKE, FAKE, FAKE, FAKE, FAKE, ws, 2, 8, 2, 0, 128, 0.1, 0, 0,
                          _lib.FA_BF16, None]
     for idx, val, status in ((7, 48, _lib.FA_ERR_INVALID_ARG),      # page_size not a power of two
                              (7, 8, _lib.FA_ERR_INVALID_ARG),       # page_size < 16
@@ -187,9 +188,9 @@ def test_decode_validation(lib):
 def test_workspace_sizes(lib):
     assert lib.fa_bwd_workspace_bytes(1, 96, 96, 8192, 128) == 2 * 96 * 8192 * 4  # D and LSE*log2(e)
     assert lib.fa_bwd_workspace_bytes(0, 1, 1, 1, 64) == 0
-    # default split: 512-row chunks -> 64 splits for a 32768-row cache
-    o_bytes = 64 * 32 * 64 * 128 * 4
-    lse_bytes = 64 * 32 * 64 * 4
+    # default split: 1024-row chunks -> 32 splits for a 32768-row cache
+    o_bytes = 64 * 32 * 32 * 128 * 4
+    lse_bytes = 64 * 32 * 32 * 4
     assert lib.fa_decode_workspace_bytes(64, 32, 8, 32768, 128, 0) == o_bytes + lse_bytes
     # one split
     assert lib.fa_decode_workspace_bytes(2, 4, 2, 100, 64, 1) == (2 * 4 * 64 * 4 + 255) // 256 * 256 + 256
