@@ -7,7 +7,7 @@ already resident in device memory:
     bf16 attention at B=1, N=8192, Hq=Hkv=96, d=128 -- the shape of the
     flash_attn fwd+bwd timing on GB200 in the zocula guide to
     flash-linear-attention (benchmark section);
-  * one KV-cache decode (fa_decode_kvcache: split kernel + merge kernel) of
+  * one KV-cache decode (fa_decode_kvcache: balanced split kernel + merge kernel) of
     64 sequences x 1 query, Hq=32, Hkv=8, d=128, cache lengths uniform in
     [1024, 32768].
 
@@ -44,6 +44,8 @@ KERNEL_SOURCES = {
     "bwd_preprocess_kernel": "fa_bwd.hip",
     "decode_split_kernel": "fa_decode.hip",
     "decode_merge_kernel": "fa_decode.hip",
+    "decode_split_bal_kernel": "fa_decode.hip",
+    "decode_merge_bal_kernel": "fa_decode.hip",
 }
 
 

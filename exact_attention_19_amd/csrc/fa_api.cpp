@@ -75,6 +75,28 @@ void decode_ws_layout(int B, int Hq, int N, int d, int num_splits, int* chunk, i
   *lse_bytes = round_up((size_t)B * Hq * (size_t)(*nsplit) * sizeof(float), 256);
 }
 
+// How a decode call splits the cache: balanced row ranges (P > 0, automatic
+// split count on a device where they apply) or fixed chunks.
+struct DecodePlan {
+  int P = 0;
+  int chunk = 0, nsplit = 0;
+  size_t o_bytes = 0, lse_bytes = 0;
+  size_t bytes() const { return o_bytes + lse_bytes; }
+};
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int N, int d, int num_splits) {
+  DecodePlan p;
+  p.P = fa::decode_balanced_ranges(B, Hq, Hkv, d, num_splits);
+  if (p.P > 0) {
+    const fa::DecodeBalLayout l = fa::decode_bal_layout(B, Hq, d, p.P);
+    p.lse_bytes = l.cum_bytes + l.lse_bytes;
+    p.o_bytes = l.o_bytes;
+  } else {
+    decode_ws_layout(B, Hq, N, d, num_splits, &p.chunk, &p.nsplit, &p.o_bytes, &p.lse_bytes);
+  }
+  return p;
+}
+
 fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
@@ -252,12 +274,8 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits) {
-  (void)Hkv;
-  if (B <= 0 || Hq <= 0 || N <= 0 || d <= 0 || num_splits < 0) return 0;
-  int chunk, nsplit;
-  size_t ob, lb;
-  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
-  return ob + lb;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0 || num_splits < 0) return 0;
+  return decode_plan(B, Hq, Hkv, N, d, num_splits).bytes();
 }
 
 fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* cache_seqlens,
@@ -274,18 +292,17 @@ fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_ca
   FA_TRY(check_ptr(fn, "cache_seqlens", cache_seqlens, 4));
   FA_TRY(check_ptr(fn, "o", o, 16));
   if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
-  int chunk, nsplit;
-  size_t ob, lb;
-  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
-  if (!workspace || workspace_bytes < ob + lb)
-    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ob + lb,
+  const DecodePlan plan = decode_plan(B, Hq, Hkv, N, d, num_splits);
+  if (!workspace || workspace_bytes < plan.bytes())
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes(),
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ob);
   fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
                    reinterpret_cast<hipStream_t>(stream)};
-  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, chunk, nsplit));
+  if (plan.P > 0) return hip_status(fn, fa::launch_decode_balanced(a, workspace, plan.P));
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes);
+  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, plan.chunk, plan.nsplit));
 }
 
 fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache, const int32_t* cache_seqlens,
@@ -324,18 +341,16 @@ fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache, con
     FA_TRY(check_ptr(fn, "v_new", v_new, 16));
   }
   if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
-  int chunk, nsplit;
-  size_t ob, lb;
-  decode_ws_layout(B, Hq, N, d, num_splits, &chunk, &nsplit, &ob, &lb);
-  if (block_table && chunk > fa::kDecodeDefaultChunk)
+  const DecodePlan plan = decode_plan(B, Hq, Hkv, N, d, num_splits);
+  if (block_table && plan.P == 0 && plan.chunk > fa::kDecodeDefaultChunk)
     return fail(FA_ERR_INVALID_ARG, "%s: with a paged cache num_splits must be 0 or >= %d", fn,
                 (N + fa::kDecodeDefaultChunk - 1) / fa::kDecodeDefaultChunk);
-  if (!workspace || workspace_bytes < ob + lb)
-    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, ob + lb,
+  if (!workspace || workspace_bytes < plan.bytes())
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes(),
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
   float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + ob);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes);
   fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
                    reinterpret_cast<hipStream_t>(stream)};
   a.block_table = block_table;
@@ -344,7 +359,8 @@ fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache, con
   a.num_pages = num_pages;
   a.k_new = k_new;
   a.v_new = v_new;
-  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, chunk, nsplit));
+  if (plan.P > 0) return hip_status(fn, fa::launch_decode_balanced(a, workspace, plan.P));
+  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, plan.chunk, plan.nsplit));
 }
 
 }  // extern "C"

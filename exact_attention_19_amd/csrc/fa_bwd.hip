@@ -581,19 +581,21 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   const int n_u = f_hi - f_lo;          // full tiles per head
   const int n1 = G * n_m;
   const int n_iter = n1 + G * n_u;
-  // Iteration it -> (query head, first query row).
-  auto tile_of = [&](int it, int& hq, int& q0) __attribute__((always_inline)) {
-    if (it < n1) {
-      const int h = uniform(it / n_m), j = it - h * n_m;
-      hq = hk * G + h;
-      q0 = (j < n_lo ? qlo + j : f_hi + (j - n_lo)) * BQ;
-    } else {
-      const int i2 = it - n1;
-      const int h = uniform(i2 / n_u), j = i2 - h * n_u;
-      hq = hk * G + h;
-      q0 = (f_lo + j) * BQ;
-    }
+  // Iteration it is tile j of head h within its phase: it = h * n_m + j in
+  // the first phase, n1 + h * n_u + j in the second. The loops visit it in
+  // order, so (h, j) is carried along and advanced by one (no divisions).
+  struct Cursor { int h, j; };
+  auto tile_at = [&](int it, Cursor c, int& hq, int& q0) __attribute__((always_inline)) {
+    hq = hk * G + c.h;
+    if (it < n1) q0 = (c.j < n_lo ? qlo + c.j : f_hi + (c.j - n_lo)) * BQ;
+    else q0 = (f_lo + c.j) * BQ;
   };
+  auto advance = [&](int it, Cursor c) __attribute__((always_inline)) {  // cursor of it + 1
+    if (it + 1 == n1) return Cursor{0, 0};
+    const int n = it < n1 ? n_m : n_u;
+    return c.j + 1 < n ? Cursor{c.h, c.j + 1} : Cursor{c.h + 1, 0};
+  };
+  Cursor cur{0, 0};
 
   const int roff = row_offset(lane);
   int toff[2];
@@ -605,9 +607,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 #pragma unroll
   for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
 
-  auto issue = [&](int it, int stage) __attribute__((always_inline)) {
+  auto issue = [&](int it, Cursor c, int stage) __attribute__((always_inline)) {
     int hq, q0;
-    tile_of(it, hq, q0);
+    tile_at(it, c, hq, q0);
     unsigned char* st = smem + stage * STAGE;
 #pragma unroll
     for (int h = 0; h < BQ / 64; ++h) {
@@ -718,9 +720,11 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 
   auto step = [&](int it, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
-    if (it + 1 < n_iter) issue(it + 1, STG ^ 1);
+    const Cursor nxt = advance(it, cur);
+    if (it + 1 < n_iter) issue(it + 1, nxt, STG ^ 1);
     int hq_unused, q0;
-    tile_of(it, hq_unused, q0);
+    tile_at(it, cur, hq_unused, q0);
+    cur = nxt;
     bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
     if (WINDOW && wr >= 0) skip = skip || q0 + BQ - 1 < kw0 - wr;
     if (WINDOW && wl >= 0) skip = skip || q0 > kw0 + 31 + wl;
@@ -731,7 +735,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
 
-  if (n_iter > 0) issue(0, 0);
+  if (n_iter > 0) issue(0, cur, 0);
   wait_vmcnt<0>();
   barrier_keep_dma();
   int it = 0;

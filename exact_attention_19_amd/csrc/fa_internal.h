@@ -96,6 +96,11 @@ struct DecodeArgs {
 constexpr int kDecodeDefaultChunk = 1024;
 // Query heads that one decode workgroup serves from a single read of K/V.
 constexpr int kDecodeMaxHeadsPerGroup = 4;
+// Balanced decode split (automatic split count): at most this many sequences
+// (their prefix sums live in LDS), and this many equal row ranges per
+// resident workgroup slot of the device.
+constexpr int kDecBalMaxB = 1024;
+constexpr int kDecBalRounds = 1;
 
 hipError_t launch_fwd(const FwdArgs& a);
 // Varlen and/or windowed forward (bf16, d = 128). a.N is ignored; a.B is
@@ -116,5 +121,16 @@ hipError_t launch_bwd(const BwdArgs& a, float* delta);
 int decode_heads_per_group(int Hq, int Hkv);
 void decode_split_plan(int N, int num_splits, int* chunk, int* nsplit);
 hipError_t launch_decode(const DecodeArgs& a, float* part_o, float* part_lse, int chunk, int nsplit);
+// Balanced split: number of row ranges P per kv-head block for these sizes on
+// the current device, or 0 when the chunked split is used instead (explicit
+// num_splits, B > kDecBalMaxB, or Hkv not a multiple of 512 / d).
+int decode_balanced_ranges(int B, int Hq, int Hkv, int d, int num_splits);
+// Workspace of the balanced split: prefix sums (B + 1 int64), then LSE and O
+// partials for P + B - 1 slots.
+struct DecodeBalLayout {
+  size_t cum_bytes, lse_bytes, o_bytes;
+};
+DecodeBalLayout decode_bal_layout(int B, int Hq, int d, int P);
+hipError_t launch_decode_balanced(const DecodeArgs& a, void* workspace, int P);
 
 }  // namespace fa

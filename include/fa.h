@@ -190,7 +190,10 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
                         int causal, int window_left, int window_right, int dtype, void* stream);
 
-/* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it). */
+/* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it).
+ * With num_splits = 0 the size depends on the current device (the balanced
+ * split described below sizes its partials by the device's resident
+ * workgroups): query it with the device current that will run the call. */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_splits);
 
 /*
@@ -207,7 +210,13 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_s
  *   o [B,Hq,d] out; lse [B,Hq] float32 out, or NULL.
  *   causal: accepted for symmetry; with one query aligned to the bottom-right
  *   corner every cached key is visible, so it does not change the result.
- *   num_splits: number of sequence splits (0 = chosen by the library from N).
+ *   num_splits: number of sequence splits (0 = chosen by the library). With
+ *     0, when Hkv is a multiple of 512 / d and B <= 1024, the valid rows of
+ *     all sequences, concatenated, are cut into equal ranges (as many as the
+ *     device has resident workgroup slots, per block of kv heads) and the
+ *     partials of each sequence are merged; otherwise each sequence is cut
+ *     into chunks of up to 1024 rows. A positive value cuts each sequence
+ *     into that many equal chunks.
  *   workspace: at least fa_decode_workspace_bytes(..., num_splits) bytes.
  * bf16 only.
  */

@@ -108,3 +108,61 @@ def test_out_of_range_lengths_give_zero_output():
     torch.cuda.synchronize()
     assert (o[:2] == 0).all() and torch.isneginf(lse[:2]).all()
     assert torch.isfinite(lse[2]).all()
+
+
+# Cases for the balanced split (automatic split count, Hkv a multiple of
+# 512 / d, B <= 1024): all sequences' rows are cut into equal ranges, so a
+# range can span many short sequences, and with few rows most ranges are
+# empty. Lengths 0 and > Lmax are invalid (output 0, LSE -inf).
+BALANCED = [
+    # B, Hq, Hkv, d, Lmax, lens
+    (5, 32, 8, 128, 16, [1, 1, 2, 1, 3]),                   # fewer rows than ranges
+    (6, 16, 8, 128, 2000, [2000, 0, 1, 5000, 1999, 37]),     # invalid lengths between valid ones
+    (3, 64, 8, 64, 900, [900, 450, 3]),                      # d = 64: 8 kv heads per wave instruction
+    (2, 8, 4, 128, 40000, [40000, 33]),                      # ranges far longer than a chunk
+]
+
+
+@pytest.mark.parametrize("case", BALANCED, ids=[f"B{c[0]}Hq{c[1]}Hkv{c[2]}d{c[3]}L{c[4]}" for c in BALANCED])
+def test_balanced_split(case):
+    fa = need_gpu()
+    B, Hq, Hkv, d, Lmax, lens = case
+    announce(f"decode balanced {case}")
+    dev = torch.device("cuda:0")
+    seed = 9 + Lmax
+    valid = [1 <= L <= Lmax for L in lens]
+    kc, vc = _make_cache(B, Lmax, Hkv, d, [L if ok else 0 for L, ok in zip(lens, valid)], seed, dev)
+    q = workloads.decode_query(B, Hq, d, seed=seed)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o, lse = fa.fa_decode_kvcache(q.to(dev), kc, vc, sl, num_splits=0)
+    o2, lse2 = fa.fa_decode_kvcache(q.to(dev), kc, vc, sl, num_splits=0)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    scale = 1 / math.sqrt(d)
+    for b in range(B):
+        if not valid[b]:
+            assert (o[b] == 0).all() and torch.isneginf(lse[b]).all(), f"seq {b}"
+            continue
+        ro, rl = _oracle_seq(q, b, lens[b], Hkv, d, seed, scale)
+        assert_bf16_close(o[b:b + 1], ro, f"O seq {b}")
+        assert_bf16_close(lse[b:b + 1], rl, f"LSE seq {b}")
+
+
+def test_many_sequences_fall_back_to_chunks():
+    """More sequences than the balanced split keeps prefix sums for: the
+    chunked split runs instead; sampled sequences against the oracle."""
+    fa = need_gpu()
+    announce("decode B=1100 chunked fallback")
+    dev = torch.device("cuda:0")
+    B, Hq, Hkv, d, Lmax = 1100, 8, 8, 128, 48
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, Lmax + 1, size=B).tolist()
+    kc, vc = _make_cache(B, Lmax, Hkv, d, lens, 21, dev)
+    q = workloads.decode_query(B, Hq, d, seed=21)
+    sl = torch.tensor(lens, dtype=torch.int32, device=dev)
+    o, lse = fa.fa_decode_kvcache(q.to(dev), kc, vc, sl)
+    torch.cuda.synchronize()
+    for b in (0, 1, 517, 1023, 1024, 1099):
+        ro, rl = _oracle_seq(q, b, lens[b], Hkv, d, 21, 1 / math.sqrt(d))
+        assert_bf16_close(o[b:b + 1], ro, f"O seq {b}")
+        assert_bf16_close(lse[b:b + 1], rl, f"LSE seq {b}")

@@ -148,3 +148,35 @@ def test_paged_full_size_decode_64_sequences():
     oc, lc = fa.fa_decode_kvcache(q, kc, vc, sl)
     torch.cuda.synchronize()
     assert torch.equal(op, oc) and torch.equal(lp, lc)
+
+
+def test_paged_long_ranges_small_pages():
+    """Balanced split with ranges longer than one page-list load (16-row
+    pages, over a thousand rows per range): paged equals contiguous bitwise,
+    and both agree with the chunked split (explicit split count) to one bf16
+    ulp."""
+    fa = need_gpu()
+    announce("decode paged long ranges, 16-row pages")
+    B, Hq, Hkv, d, ps = 2, 16, 4, 128, 16
+    lens = [600000, 100000]
+    N = 600016
+    mp = N // ps
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    kc = torch.randn((B, N, Hkv, d), generator=gen, device=DEV).to(torch.bfloat16)
+    vc = torch.randn((B, N, Hkv, d), generator=gen, device=DEV).to(torch.bfloat16)
+    perm = torch.randperm(B * mp, generator=torch.Generator().manual_seed(4))
+    table = torch.argsort(perm).view(B, mp).to(torch.int32).to(DEV)
+    kp = torch.empty((B * mp, ps, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    vp = torch.empty_like(kp)
+    kp[table.view(-1).long()] = kc.view(B * mp, ps, Hkv, d)
+    vp[table.view(-1).long()] = vc.view(B * mp, ps, Hkv, d)
+    q = torch.randn((B, Hq, d), generator=gen, device=DEV).to(torch.bfloat16)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    op, lp = fa.fa_decode_kvcache_ext(q, kp, vp, sl, block_table=table)
+    oc, lc = fa.fa_decode_kvcache(q, kc, vc, sl)
+    os_, ls_ = fa.fa_decode_kvcache(q, kc, vc, sl, num_splits=600)
+    torch.cuda.synchronize()
+    assert torch.equal(op, oc) and torch.equal(lp, lc)
+    ulp = (os_.float().abs() * 2.0 ** -7).clamp_min(1e-30)
+    assert ((os_.float() - oc.float()).abs() <= ulp + 1e-6).all()
+    assert ((ls_ - lc).abs() <= 1e-4).all()
