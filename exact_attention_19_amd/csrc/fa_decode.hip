@@ -558,11 +558,15 @@ __global__ __launch_bounds__(kDecThreads) void decode_split_bal_kernel(
 
 // Merge for the balanced split: output (b, hq) combines the partials at
 // slots p + b of the ranges p that overlap sequence b (empty ranges skipped).
+// One wave: 64 slots at a time, lane i holding slot p_first + i; the LSE max
+// and the weights come from wave reductions, and each lane then sums its
+// D / 64 output dims over the slots with independent loads.
 template <int D>
 __global__ __launch_bounds__(64) void decode_merge_bal_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, const long long* __restrict__ cum,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int P) {
   constexpr int PER = D / 64;
+  __shared__ float sm_w[64];
   const int bh = blockIdx.x;
   const int b = bh / Hq, hq = bh - b * Hq;
   const int tid = threadIdx.x;
@@ -579,22 +583,35 @@ __global__ __launch_bounds__(64) void decode_merge_bal_kernel(
   const int p_first = (int)min((long long)P - 1, ((c0 + 1) * P - 1) / R);
   const int p_last = (int)min((long long)P - 1, (c1 * P - 1) / R);
   auto r_of = [&](int p) { return (long long)p * R / P; };
+  auto slot_lse = [&](int p) {  // -inf for ranges past p_last or empty
+    if (p > p_last || r_of(p) == r_of(p + 1)) return kNegInf;
+    return part_lse[((int64_t)p + b) * Hq + hq];
+  };
   float mm = kNegInf;
-  for (int p = p_first; p <= p_last; ++p) {
-    if (r_of(p) == r_of(p + 1)) continue;
-    mm = fmaxf(mm, part_lse[((int64_t)p + b) * Hq + hq]);
-  }
+  for (int p0 = p_first; p0 <= p_last; p0 += 64) mm = fmaxf(mm, slot_lse(p0 + tid));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
   float wsum = 0.f;
   float os[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) os[i] = 0.f;
-  for (int p = p_first; p <= p_last; ++p) {
-    if (r_of(p) == r_of(p + 1)) continue;
-    const int64_t ps = ((int64_t)p + b) * Hq + hq;
-    const float w = fast_exp2(part_lse[ps] - mm);
-    wsum += w;
+  for (int p0 = p_first; p0 <= p_last; p0 += 64) {
+    const float w = fast_exp2(slot_lse(p0 + tid) - mm);  // 0 for empty or absent slots
+    float ws = w;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) os[i] = fmaf(w, part_o[ps * D + tid * PER + i], os[i]);
+    for (int off = 32; off > 0; off >>= 1) ws += __shfl_xor(ws, off, 64);
+    wsum += ws;
+    __syncthreads();
+    sm_w[tid] = w;
+    __syncthreads();
+    const int n = min(64, p_last - p0 + 1);
+    for (int i = 0; i < n; ++i) {
+      const float wi = sm_w[i];
+      if (wi == 0.f) continue;
+      const float* po = part_o + (((int64_t)p0 + i + b) * Hq + hq) * D + tid * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) os[e] = fmaf(wi, po[e], os[e]);
+    }
   }
   const float inv = 1.f / wsum;
 #pragma unroll
