@@ -179,7 +179,8 @@ def _pairs_band(nq, nk, causal, wl=-1, wr=-1):
 
 
 def extras(fa_mod, lib, dev):
-    """Secondary lines: the sliding-window, varlen, paged-decode and
+    """Secondary lines: the causal forward sweep and GQA fwd+bwd of the
+    workload configs, and the sliding-window, varlen, paged-decode and
     block-sparse paths on workloads of the pages' shapes. Each rate uses the
     algorithmic work (4*d FLOP per visible query-key pair in a forward,
     2.5x that in a backward; bytes read once for decode)."""
@@ -189,6 +190,33 @@ def extras(fa_mod, lib, dev):
     import workloads
 
     out = {}
+    # Causal forward sweep: hidden 2048 (16 heads x 128), 16k tokens per batch.
+    sweep = {}
+    for N in (512, 2048, 8192, 16384):
+        B = 16384 // N
+        inp = workloads.prefill_inputs(B, N, 16, 16, 128, "bf16", seed=5, mult=0.5)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        del inp
+        ms = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=True), reps=10, warm=5)
+        pairs = _pairs_band(N, N, True) * B * 16
+        tf = 4 * 128 * pairs / (ms * 1e9)
+        sweep[f"N={N} B={B}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del q, k, v
+    out["fwd_sweep_h2048"] = {"workload": "causal forward, H=16 d=128, B*N = 16384 tokens", "points": sweep}
+    # Forward + backward with GQA (Hkv = 12) at the GB200 timing shape.
+    B, N, H, Hkv, d = 1, 8192, 96, 12, 128
+    inp = workloads.prefill_inputs(B, N, H, Hkv, d, "bf16", seed=6, with_do=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    del inp
+    o, lse = fa_mod.fa_fwd(q, k, v, causal=True)
+    pairs = _pairs_band(N, N, True) * B * H
+    ms_f = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=True), reps=10, warm=5)
+    ms_b = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True), reps=10, warm=5)
+    out["gqa_fwd_bwd"] = {"workload": f"B={B} N={N} Hq={H} Hkv={Hkv} d={d} causal", "fwd_ms": round(ms_f, 4),
+                          "bwd_ms": round(ms_b, 4),
+                          "fwd+bwd TFLOP/s": round(3.5 * 4 * d * pairs / ((ms_f + ms_b) * 1e9), 1),
+                          "note": "fa_bwd: preprocess + dK/dV + dQ kernels"}
+    del q, k, v, do, o, lse
     # Sliding window at the GB200 timing shape, window of 4096 keys (causal).
     B, N, H, d = 1, 8192, 96, 128
     wl = 4095
