@@ -527,9 +527,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   if (BHK % 8 == 0) {
     // Workgroups are dealt round-robin to the 8 XCDs: keep every key tile of
     // kv head h on XCD h % 8, so the query tiles they all stream share its L2.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    bhk = (slot / nkt) * 8 + xcd;
-    kt = slot % nkt;
+    xcd_order(blockIdx.x, BHK, nkt, kDkdvHeadGroup, bhk, kt);
   } else {
     bhk = blockIdx.x % BHK;
     kt = blockIdx.x / BHK;  // low key tiles see the most query tiles: launched first
@@ -790,9 +788,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   if (BH % 8 == 0) {
     // Every query tile of head h on XCD h % 8 (workgroups are dealt
     // round-robin to the XCDs), so the K/V tiles they stream share its L2.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    bh = (slot / num_q_tiles) * 8 + xcd;
-    rank = slot % num_q_tiles;
+    xcd_order(blockIdx.x, BH, num_q_tiles, kDqHeadGroup, bh, rank);
   } else {
     bh = blockIdx.x % BH;
     rank = blockIdx.x / BH;

@@ -148,6 +148,28 @@ __device__ __forceinline__ bf16x8 load_tr_operand(const __bf16* tr, int d, int s
   return *reinterpret_cast<const bf16x8*>(tr + d * 64 + u * 8);
 }
 
+// Workgroup order for a launch of nh x T workgroups (nh heads, a multiple of
+// 8, each with T tiles; rank 0 is a head's heaviest tile). Workgroups are
+// dealt round-robin to the 8 XCDs, so workgroup bid runs on XCD bid % 8; that
+// XCD takes heads xcd, xcd + 8, ..., so its L2 only ever holds their tiles.
+// It visits them in groups of `group` heads, rank-major inside a group (the
+// heaviest tile of every head in the group first), so that the heaviest tile
+// of the last head is not dispatched when little other work is left.
+// group = 1 is plain head-major order.
+__device__ __forceinline__ void xcd_order(int bid, int nh, int T, int group, int& h, int& rank) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int grp = slot / (group * T);
+  const int g = min(group, (nh >> 3) - grp * group);  // heads in this group
+  const int w = slot - grp * group * T;
+  rank = w / g;
+  h = (grp * group + (w - rank * g)) * 8 + xcd;
+}
+
+// Heads per group in xcd_order, per kernel.
+constexpr int kFwdHeadGroup = 4;
+constexpr int kDkdvHeadGroup = 4;
+constexpr int kDqHeadGroup = 8;
+
 // ---------------------------------------------------------------------------
 // Row-major 64 x 128 bf16 tiles in LDS (256 bytes per row), filled straight
 // from global memory with global_load_lds_dwordx4: one wave instruction

@@ -317,9 +317,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   if (BH % 8 == 0) {
     // Workgroups are dealt round-robin to the 8 XCDs; give each XCD whole
     // heads (every query tile of head h on XCD h % 8) so its L2 holds them.
-    const int xcd = bid & 7, slot = bid >> 3;
-    bh = (slot / num_q_tiles) * 8 + xcd;
-    rank = slot % num_q_tiles;
+    xcd_order(bid, BH, num_q_tiles, kFwdHeadGroup, bh, rank);
   } else {
     bh = bid % BH;
     rank = bid / BH;
