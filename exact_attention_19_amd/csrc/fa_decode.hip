@@ -605,12 +605,25 @@ __global__ __launch_bounds__(64) void decode_merge_bal_kernel(
     sm_w[tid] = w;
     __syncthreads();
     const int n = min(64, p_last - p0 + 1);
-    for (int i = 0; i < n; ++i) {
-      const float wi = sm_w[i];
-      if (wi == 0.f) continue;
-      const float* po = part_o + (((int64_t)p0 + i + b) * Hq + hq) * D + tid * PER;
+    // Eight slots per batch, all loads issued before any is used. Indices
+    // past n re-read slot n - 1 (in bounds) and get weight 0; a slot of
+    // weight 0 (empty range, never written) is excluded by a select, so
+    // whatever its memory holds cannot reach the sum.
+    for (int i0 = 0; i0 < n; i0 += 8) {
+      float v[8][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) os[e] = fmaf(wi, po[e], os[e]);
+      for (int u = 0; u < 8; ++u) {
+        const int i = min(i0 + u, n - 1);
+        const float* po = part_o + (((int64_t)p0 + i + b) * Hq + hq) * D + tid * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[u][e] = po[e];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wi = i0 + u < n ? sm_w[i0 + u] : 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) os[e] = wi != 0.f ? fmaf(wi, v[u][e], os[e]) : os[e];
+      }
     }
   }
   const float inv = 1.f / wsum;
