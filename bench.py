@@ -284,7 +284,7 @@ def extras(fa_mod, lib, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(pass --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
