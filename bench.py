@@ -179,8 +179,8 @@ def _pairs_band(nq, nk, causal, wl=-1, wr=-1):
 
 
 def extras(fa_mod, lib, dev):
-    """Secondary lines: the causal forward sweep and GQA fwd+bwd of the
-    workload configs, and the sliding-window, varlen, paged-decode and
+    """Secondary lines: the causal forward sweep, the two small forward
+    configs and GQA fwd+bwd of the workload configs, and the sliding-window, varlen, paged-decode and
     block-sparse paths on workloads of the pages' shapes. Each rate uses the
     algorithmic work (4*d FLOP per visible query-key pair in a forward,
     2.5x that in a backward; bytes read once for decode)."""
@@ -188,6 +188,7 @@ def extras(fa_mod, lib, dev):
     import torch
 
     import workloads
+    from exact_attention_19_amd import _lib
 
     out = {}
     # Causal forward sweep: hidden 2048 (16 heads x 128), 16k tokens per batch.
@@ -203,6 +204,26 @@ def extras(fa_mod, lib, dev):
         sweep[f"N={N} B={B}"] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
         del q, k, v
     out["fwd_sweep_h2048"] = {"workload": "causal forward, H=16 d=128, B*N = 16384 tokens", "points": sweep}
+    # The two small configs: an fp32 forward (B=1, H=1, N=128, d=64, non-causal)
+    # and a bf16 d=64 forward (B=2, H=8, N=1024, non-causal and causal). Both
+    # are a few workgroups and launch-bound; they are timed through the C ABI
+    # directly (the torch binding's per-call checks would dominate).
+    small = {}
+    for name, (B, N, H, d, dt, causal) in {"fp32 B=1 H=1 N=128 d=64": (1, 128, 1, 64, "fp32", False),
+                                           "bf16 B=2 H=8 N=1024 d=64": (2, 1024, 8, 64, "bf16", False),
+                                           "bf16 B=2 H=8 N=1024 d=64 causal": (2, 1024, 8, 64, "bf16", True)}.items():
+        inp = workloads.prefill_inputs(B, N, H, H, d, dt, seed=0)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        sp = torch.cuda.current_stream(dev).cuda_stream
+        args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, N, d,
+                1.0 / d ** 0.5, int(causal), _lib.FA_FP32 if dt == "fp32" else _lib.FA_BF16, sp)
+        ms = _time_ms(lambda: _lib.check(lib.fa_fwd(*args)), reps=50, warm=10)
+        pairs = _pairs_band(N, N, causal) * B * H
+        small[name] = {"ms": round(ms, 4), "TFLOP/s": round(4 * d * pairs / (ms * 1e9), 2)}
+        del inp, q, k, v, o, lse
+    out["small_configs_fwd"] = small
     # Forward + backward with GQA (Hkv = 12) at the GB200 timing shape.
     B, N, H, Hkv, d = 1, 8192, 96, 12, 128
     inp = workloads.prefill_inputs(B, N, H, Hkv, d, "bf16", seed=6, with_do=True)
