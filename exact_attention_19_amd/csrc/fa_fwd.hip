@@ -747,36 +747,46 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   }
 }
 
-// fp32 path: one query row per lane, 32-key tiles staged in LDS.
+// fp32 path: eight query rows per wave, eight lanes per row. Each lane keeps
+// D / 8 consecutive dimensions of its row's query and output accumulator; a
+// score is the sum of the eight lanes' partial dot products (xor shuffles
+// inside the lane group), so every lane of the group holds the same score and
+// softmax state. 32-key tiles of K and V are staged in LDS.
 template <int D>
-__global__ __launch_bounds__(64, 1) void fwd_f32_kernel(
+__global__ __launch_bounds__(256) void fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
     int causal, int num_q_tiles) {
+  constexpr int LP = 8, DL = D / LP;  // lanes per row, dimensions per lane
+  constexpr int BMQ = 32;             // query rows per workgroup (4 waves x 8)
   constexpr int TK = 32;
-  __shared__ float ks[TK][D];
-  __shared__ float vs[TK][D];
+  __shared__ __align__(16) float ks[TK][D];
+  __shared__ __align__(16) float vs[TK][D];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int part = lane % LP;
   const int bh = blockIdx.x % (B * Hq);
   const int qt = blockIdx.x / (B * Hq);
   const int b = bh / Hq, hq = bh % Hq, hk = hq / (Hq / Hkv);
-  const int my_q = qt * 64 + tid;
+  const int my_q = qt * BMQ + wave * (64 / LP) + lane / LP;
   const int64_t qs = (int64_t)Hq * D, kvs = (int64_t)Hkv * D;
-  const float* qrow = q + ((int64_t)b * N + min(my_q, N - 1)) * qs + (int64_t)hq * D;
-  float qr[D], acc[D];
+  const float* qrow = q + ((int64_t)b * N + min(my_q, N - 1)) * qs + (int64_t)hq * D + part * DL;
+  float qr[DL], acc[DL];
 #pragma unroll
-  for (int c = 0; c < D; ++c) { qr[c] = qrow[c]; acc[c] = 0.f; }
+  for (int c = 0; c < DL; ++c) { qr[c] = qrow[c]; acc[c] = 0.f; }
   float m_run = kNegInf, l_run = 0.f;
   int kv_end = N;
-  if (causal) kv_end = min(N, qt * 64 + 64);
+  if (causal) kv_end = min(N, qt * BMQ + BMQ);
   for (int k0 = 0; k0 < kv_end; k0 += TK) {
     __syncthreads();
-    for (int i = tid; i < TK * D; i += 64) {
-      const int r = i / D, c = i % D;
+    for (int i = tid; i < TK * D / 4; i += 256) {
+      const int r = i / (D / 4), c4 = i % (D / 4);
       const int key = k0 + r;
-      const int64_t off = ((int64_t)b * N + key) * kvs + (int64_t)hk * D + c;
-      ks[r][c] = key < N ? k[off] : 0.f;
-      vs[r][c] = key < N ? v[off] : 0.f;
+      const int64_t off = ((int64_t)b * N + min(key, N - 1)) * kvs + (int64_t)hk * D + 4 * c4;
+      const float4 kv4 = *reinterpret_cast<const float4*>(k + off);
+      const float4 vv4 = *reinterpret_cast<const float4*>(v + off);
+      *reinterpret_cast<float4*>(&ks[r][4 * c4]) = key < N ? kv4 : float4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4*>(&vs[r][4 * c4]) = key < N ? vv4 : float4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
     float s[TK];
@@ -785,7 +795,9 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(
     for (int j = 0; j < TK; ++j) {
       float dot = 0.f;
 #pragma unroll
-      for (int c = 0; c < D; ++c) dot = fmaf(qr[c], ks[j][c], dot);
+      for (int c = 0; c < DL; ++c) dot = fmaf(qr[c], ks[j][part * DL + c], dot);
+#pragma unroll
+      for (int w = 1; w < LP; w <<= 1) dot += __shfl_xor(dot, w, 64);
       const int key = k0 + j;
       const bool masked = key >= N || (causal && key > my_q);
       s[j] = masked ? kNegInf : dot * scale_log2;
@@ -797,22 +809,22 @@ __global__ __launch_bounds__(64, 1) void fwd_f32_kernel(
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] *= alpha;
+    for (int c = 0; c < DL; ++c) acc[c] *= alpha;
 #pragma unroll
     for (int j = 0; j < TK; ++j) {
       const float p = exp2f(s[j] - m_use);
       l_run += p;
 #pragma unroll
-      for (int c = 0; c < D; ++c) acc[c] = fmaf(p, vs[j][c], acc[c]);
+      for (int c = 0; c < DL; ++c) acc[c] = fmaf(p, vs[j][part * DL + c], acc[c]);
     }
   }
   if (my_q < N) {
     const bool empty = !(l_run > 0.f);
     const float inv = empty ? 0.f : 1.f / l_run;
-    float* orow = o + ((int64_t)b * N + my_q) * qs + (int64_t)hq * D;
+    float* orow = o + ((int64_t)b * N + my_q) * qs + (int64_t)hq * D + part * DL;
 #pragma unroll
-    for (int c = 0; c < D; ++c) orow[c] = acc[c] * inv;
-    lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + log2f(l_run)) * kLn2;
+    for (int c = 0; c < DL; ++c) orow[c] = acc[c] * inv;
+    if (part == 0) lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + log2f(l_run)) * kLn2;
   }
 }
 
@@ -856,10 +868,10 @@ hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
 
 template <int D>
 hipError_t launch_f32(const FwdArgs& a) {
-  const int num_q_tiles = (a.N + 63) / 64;
+  const int num_q_tiles = (a.N + 31) / 32;
   const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(64), 0, a.stream,
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3((unsigned)grid), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                      a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, a.causal, num_q_tiles);
   return hipGetLastError();
