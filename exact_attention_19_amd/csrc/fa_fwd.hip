@@ -725,6 +725,37 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
 
   if (!wave_active) return;
   const int64_t lse_base = VARLEN ? (int64_t)hq * seq.total_q + q_start : ((int64_t)b * Hq + hq) * N;
+  if constexpr (QB == 1) {
+    // The wave's 32 x 128 output tile goes out through LDS (the tile ring is
+    // free: every wave has passed the last barrier), so the global stores
+    // are 16 bytes per lane over whole 256-byte rows instead of 8-byte
+    // pieces of 32 rows. Lane (l32, hh) holds row l32, dims 32 db + 8 i +
+    // 4 hh .. + 3; unit u = 4 db + i of the row lands at u ^ tile_swz(row).
+    const float l_tot = pair_sum(l_run[0]);
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    unsigned char* ot = smem + wave * 8192;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[0][db][4 * i + 0] * inv, oacc[0][db][4 * i + 1] * inv);
+        w[1] = pack_bf16x2(oacc[0][db][4 * i + 2] * inv, oacc[0][db][4 * i + 3] * inv);
+        *reinterpret_cast<u32x2*>(ot + l32 * 256 + 16 * ((4 * db + i) ^ tile_swz(l32)) + 8 * hh) = w;
+      }
+    }
+    const int unit = lane & 15;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int row = 4 * c + (lane >> 4);
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ot + row * 256 + 16 * (unit ^ tile_swz(row)));
+      if (qw0 + row < Nq)
+        *reinterpret_cast<u32x4*>(o + ((int64_t)q_start + qw0 + row) * q_rs + (int64_t)hq * D + 8 * unit) = val;
+    }
+    if (hh == 0 && my_q[0] < Nq) lse[lse_base + my_q[0]] = empty ? kNegInf : (m_run[0] + __log2f(l_tot)) * kLn2;
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < QB; ++j) {
     const float l_tot = pair_sum(l_run[j]);
