@@ -126,3 +126,52 @@ def test_decode_64_sequences_32k_cache():
         ro, rl = oracle.attn_decode(f64(qd[b:b + 1]), f64(kr)[None], f64(vr)[None], np.array([L]), w.scale)
         assert_bf16_close(o[b:b + 1].cpu(), ro, f"O seq {b} (L={L})")
         assert_bf16_close(lse[b:b + 1].cpu(), rl, f"LSE seq {b} (L={L})")
+
+
+def test_window_4095_forward_backward_full_size():
+    """The sliding-window workload of the benchmark (B=1, N=8192, H=96, d=128,
+    causal, window (4095, 0)): every output finite, and one head's O, LSE,
+    dQ, dK, dV against the oracle's full forward and backward of that head."""
+    fa = need_gpu()
+    announce("large window fwd+bwd B1 N8192 H96 w4095")
+    B, N, H, d, win = 1, 8192, 96, 128, (4095, 0)
+    scale = 1 / math.sqrt(d)
+    inp = workloads.prefill_inputs(B, N, H, H, d, "bf16", seed=7, with_do=True)
+    dev = torch.device("cuda:0")
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd_window(q, k, v, win, scale=scale, causal=True)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=scale, causal=True, window=win)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t).all()
+    h = H - 1
+    sl = slice(h, h + 1)
+    args = [f64(inp[n][:, :, sl]) for n in ("q", "k", "v")]
+    ro, rl = oracle.attn_fwd(*args, scale, True, window=win)
+    assert_bf16_close(o[:, :, sl].cpu(), ro, "O")
+    assert_bf16_close(lse[:, sl].cpu(), rl, "LSE")
+    rdq, rdk, rdv, _ = oracle.attn_bwd(*args, f64(inp["do"][:, :, sl]), scale, True, window=win)
+    assert_bf16_close(dq[:, :, sl].cpu(), rdq, "dQ")
+    assert_bf16_close(dk[:, :, sl].cpu(), rdk, "dK")
+    assert_bf16_close(dv[:, :, sl].cpu(), rdv, "dV")
+
+
+def test_varlen_benchmark_batch():
+    """The varlen workload of the benchmark: sequences U[256, 4096] packed to
+    at least 16k tokens, H=16, d=128, causal; all 16 heads against the oracle's
+    varlen forward."""
+    fa = need_gpu()
+    announce("large varlen fwd U[256,4096] H16")
+    rng = np.random.default_rng(2)
+    lens = []
+    while sum(lens) < 16384:
+        lens.append(int(rng.integers(256, 4097)))
+    vin = workloads.varlen_inputs(lens, lens, 16, 16, 128, seed=3)
+    dev = torch.device("cuda:0")
+    q, k, v = (vin[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = fa.fa_fwd_varlen(q, k, v, vin["cu_q"].to(dev), vin["cu_k"].to(dev), max(lens), causal=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd_varlen(f64(vin["q"]), f64(vin["k"]), f64(vin["v"]), vin["cu_q"].numpy(),
+                                    vin["cu_k"].numpy(), 1 / math.sqrt(128), True)
+    assert_bf16_close(o.cpu(), ro, "O")
+    assert_bf16_close(lse.cpu(), rl, "LSE")
