@@ -120,6 +120,8 @@ BALANCED = [
     (6, 16, 8, 128, 2000, [2000, 0, 1, 5000, 1999, 37]),     # invalid lengths between valid ones
     (3, 64, 8, 64, 900, [900, 450, 3]),                      # d = 64: 8 kv heads per wave instruction
     (2, 8, 4, 128, 40000, [40000, 33]),                      # ranges far longer than a chunk
+    (4, 8, 8, 128, 3000, [3000, 1, 2500, 17]),               # one query head per kv head
+    (3, 64, 4, 128, 5000, [5000, 4096, 1]),                  # 16 query heads per kv head
 ]
 
 
