@@ -506,9 +506,98 @@ def pin_blocksparse_properties(m):
                     np.testing.assert_allclose(lse[b, h, i], math.log(tot), rtol=0, atol=1e-12)
 
 
+def _brute_bwd(q, k, v, do, scale, causal, window=(-1, -1)):
+    """Scalar-loop gradients of sum(O * dO), the window condition written out.
+
+    For each (batch, query head, row) the visible keys are collected with the
+    same rule as the scalar forward above; p_j = exp(s_j) / sum exp(s), then
+    dV_j += p_j dO_i, dp_j = dO_i . V_j, D_i = sum_j p_j dp_j,
+    ds_j = p_j (dp_j - D_i), dQ_i = scale sum_j ds_j K_j, dK_j += scale ds_j Q_i.
+    """
+    B, nq, hq, d = q.shape
+    nk, hkv = k.shape[1], k.shape[2]
+    g = hq // hkv
+    dq, dk, dv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
+    for b in range(B):
+        for h in range(hq):
+            kh = h // g
+            for i in range(nq):
+                diag = i + (nk - nq)
+                vis = []
+                for j in range(nk):
+                    if causal and j > diag:
+                        continue
+                    if window[0] >= 0 and j < diag - window[0]:
+                        continue
+                    if window[1] >= 0 and j > diag + window[1]:
+                        continue
+                    vis.append((j, scale * sum(q[b, i, h, c] * k[b, j, kh, c] for c in range(d))))
+                if not vis:
+                    continue
+                top = max(sv for _, sv in vis)
+                tot = sum(math.exp(sv - top) for _, sv in vis)
+                pj = [(j, math.exp(sv - top) / tot) for j, sv in vis]
+                dpj = {j: sum(do[b, i, h, c] * v[b, j, kh, c] for c in range(d)) for j, _ in pj}
+                big_d = sum(p * dpj[j] for j, p in pj)
+                for j, p in pj:
+                    ds = p * (dpj[j] - big_d)
+                    for c in range(d):
+                        dv[b, j, kh, c] += p * do[b, i, h, c]
+                        dq[b, i, h, c] += scale * ds * k[b, j, kh, c]
+                        dk[b, j, kh, c] += scale * ds * q[b, i, h, c]
+    return dq, dk, dv
+
+
+BWD_WINDOW_CASES = [(0, 0), (1, 0), (2, -1), (-1, 2), (3, 1)]
+
+
+def pin_window_bwd_brute_force(m):
+    """Backward with windows (and without) against the scalar loops above, GQA
+    and Nq != Nk included, causal and non-causal."""
+    rng = np.random.default_rng(26)
+    for (B, nq, nk, hq, hkv, d) in BRUTE_SHAPES[1:5]:
+        q, k, v = _rand(rng, B, nq, hq, d), _rand(rng, B, nk, hkv, d), _rand(rng, B, nk, hkv, d)
+        do = _rand(rng, B, nq, hq, d)
+        for window in [(-1, -1)] + BWD_WINDOW_CASES:
+            for causal in (False, True):
+                dq, dk, dv, _ = m.attn_bwd(q, k, v, do, 0.55, causal, window)
+                bq, bk, bv = _brute_bwd(q, k, v, do, 0.55, causal, window)
+                for got, want in ((dq, bq), (dk, bk), (dv, bv)):
+                    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12, err_msg=f"{window} {causal}")
+
+
+def pin_window_finite_differences(m):
+    """Central differences of sum(O * dO) through the windowed forward (itself
+    pinned by brute force) against the windowed backward, with GQA."""
+    rng = np.random.default_rng(27)
+    h = 1e-6
+    for (B, nq, nk, hq, hkv, d) in [(1, 5, 5, 4, 2, 3), (1, 4, 6, 2, 1, 2)]:
+        q, k, v = _rand(rng, B, nq, hq, d), _rand(rng, B, nk, hkv, d), _rand(rng, B, nk, hkv, d)
+        do = _rand(rng, B, nq, hq, d)
+        for window in BWD_WINDOW_CASES:
+            for causal in (False, True):
+                grads = dict(zip("qkv", m.attn_bwd(q, k, v, do, 0.6, causal, window)[:3]))
+                base = {"q": q, "k": k, "v": v}
+
+                def loss(args):
+                    return float((m.attn_fwd(args["q"], args["k"], args["v"], 0.6, causal, window)[0] * do).sum())
+
+                for name in "qkv":
+                    x = base[name]
+                    num = np.zeros_like(x)
+                    for idx in np.ndindex(*x.shape):
+                        xp, xm = x.copy(), x.copy()
+                        xp[idx] += h
+                        xm[idx] -= h
+                        num[idx] = (loss({**base, name: xp}) - loss({**base, name: xm})) / (2 * h)
+                    err = np.abs(num - grads[name]).max() / max(1.0, np.abs(grads[name]).max())
+                    assert err < 1e-6, (name, window, causal, err)
+
+
 PINS += [pin_golden_window, pin_golden_varlen, pin_window_brute_force, pin_window_special_cases,
          pin_varlen_is_per_sequence_dense, pin_golden_decode_paged, pin_paged_decode_properties,
-         pin_golden_blocksparse, pin_blocksparse_properties]
+         pin_golden_blocksparse, pin_blocksparse_properties, pin_window_bwd_brute_force,
+         pin_window_finite_differences]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -561,6 +650,10 @@ MUTANTS = {
     "blocksparse_block_off_by_one": ("bm[np.arange(nq)[:, None] // block, np.arange(nk)[None, :] // block]",
                                      "bm[np.arange(nq)[:, None] // block, np.minimum(np.arange(nk)[None, :] + 1, nk - 1) // block]"),
     "blocksparse_mask_ignored": ("        s = np.where(keep_extra, s, -np.inf)", "        s = s"),
+    "bwd_window_dropped": ("_, p, _ = head_probs(qh, kk, scale, causal, window=window)",
+                           "_, p, _ = head_probs(qh, kk, scale, causal)"),
+    "bwd_window_left_only": ("_, p, _ = head_probs(qh, kk, scale, causal, window=window)",
+                             "_, p, _ = head_probs(qh, kk, scale, causal, window=(window[0], -1))"),
     "varlen_lse_row_major": ("lse[:, q0:q1] = lb[0]", "lse[:, q0:q1] = lb[0][::-1] if lb.shape[1] > 1 else lb[0]"),
 }
 
