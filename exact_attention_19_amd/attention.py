@@ -60,15 +60,18 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     _check_tensor("lse", lse, torch.float32, 3, q.device)
+    if out.shape != q.shape or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse shapes do not match q")
     st = _lib.load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale,
                             int(bool(causal)), _DT[q.dtype], _stream(q.device))
     _lib.check(st)
     return out, lse
 
 
-def fa_fwd_window(q, k, v, window, scale=None, causal=False):
+def fa_fwd_window(q, k, v, window, scale=None, causal=False, out=None, lse=None):
     """Sliding-window forward (bf16, d = 128): window = (left, right), -1 is
-    unbounded on that side. Returns (o, lse) laid out as fa_fwd."""
+    unbounded on that side. Returns (o, lse) laid out as fa_fwd, written into
+    out / lse when given."""
     _check_tensor("q", q, torch.bfloat16, 4)
     _check_tensor("k", k, torch.bfloat16, 4, q.device)
     _check_tensor("v", v, torch.bfloat16, 4, q.device)
@@ -78,8 +81,12 @@ def fa_fwd_window(q, k, v, window, scale=None, causal=False):
     Hkv = k.shape[2]
     wl, wr = (int(x) for x in window)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q)
-    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, torch.bfloat16, 4, q.device)
+    _check_tensor("lse", lse, torch.float32, 3, q.device)
+    if out.shape != q.shape or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("out/lse shapes do not match q")
     st = _lib.load().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, N, d, scale,
                                    int(bool(causal)), wl, wr, _lib.FA_BF16, _stream(q.device))
     _lib.check(st)
@@ -143,9 +150,10 @@ def fa_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False):
     return out, lse
 
 
-def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1)):
-    """Attention backward from the forward's O and LSE. Returns (dq, dk, dv).
-    A window other than (-1, -1) calls fa_bwd_window (d = 128)."""
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=None, dk=None, dv=None):
+    """Attention backward from the forward's O and LSE. Returns (dq, dk, dv),
+    written into the given tensors when passed. A window other than (-1, -1)
+    calls fa_bwd_window (d = 128)."""
     _check_tensor("q", q, torch.bfloat16, 4)
     dev = q.device
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -159,9 +167,14 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1)):
     lib = _lib.load()
     ws_bytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    dq = torch.empty_like(q)
-    dk = torch.empty_like(k)
-    dv = torch.empty_like(v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dq", dq, torch.bfloat16, 4, dev)
+    _check_tensor("dk", dk, torch.bfloat16, 4, dev)
+    _check_tensor("dv", dv, torch.bfloat16, 4, dev)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq/dk/dv must have the shapes of q/k/v")
     wl, wr = (int(x) for x in window)
     if wl < 0 and wr < 0:
         st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),

@@ -1019,12 +1019,6 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   }
 }
 
-template <typename K>
-hipError_t set_smem(K kern, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
-}
-
 template <int D, bool CAUSAL, bool WINDOW = false>
 hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const float scale_log2 = a.scale * kLog2e;
@@ -1045,7 +1039,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       constexpr int BQ = kDkdvQueryTile;
       auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>;
       constexpr size_t smem = 2 * (2 * BQ * 256 + 8 * BQ);
-      hipError_t e = set_smem(kern, smem);
+      hipError_t e = set_smem_once(kern, smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1054,7 +1048,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       return hipGetLastError();
     }
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
-    hipError_t e = set_smem(kern, DkdvSmem<D>::BYTES);
+    hipError_t e = set_smem_once(kern, DkdvSmem<D>::BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DkdvSmem<D>::BYTES, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
@@ -1068,7 +1062,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   if (D == 128) {
     auto kern = bwd_dq_d128_kernel<CAUSAL, WINDOW>;
     constexpr size_t smem = 2 * 2 * 64 * 256;
-    hipError_t e = set_smem(kern, smem);
+    hipError_t e = set_smem_once(kern, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1077,7 +1071,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
     return hipGetLastError();
   }
   auto kern = bwd_dq_kernel<D, CAUSAL>;
-  hipError_t e = set_smem(kern, DqSmem<D>::BYTES);
+  hipError_t e = set_smem_once(kern, DqSmem<D>::BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,

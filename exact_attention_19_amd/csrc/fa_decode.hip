@@ -744,9 +744,9 @@ const void* bal_kernel_ptr() {
 
 // Resident workgroups of the balanced split kernel per CU, cached per device.
 int bal_slots_per_cu(int dev, int d, int gp) {
-  static std::atomic<int> cache[16][2][3];
+  static std::atomic<int> cache[kMaxDevices][2][3];
   const int di = d == 64 ? 0 : 1, gi = gp == 1 ? 0 : (gp == 2 ? 1 : 2);
-  if (dev < 0 || dev >= 16) return 0;
+  if (dev < 0 || dev >= kMaxDevices) return 0;
   int v = cache[dev][di][gi].load(std::memory_order_relaxed);
   if (v > 0) return v;
   const void* k = d == 64 ? (gp == 1 ? bal_kernel_ptr<64, 1>() : gp == 2 ? bal_kernel_ptr<64, 2>() : bal_kernel_ptr<64, 4>())

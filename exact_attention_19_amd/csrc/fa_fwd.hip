@@ -867,8 +867,7 @@ hipError_t launch_bf16(const FwdArgs& a) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t smem = FwdSmem<D, NWAVES>::BYTES;
   auto kern = fwd_bf16_kernel<D, NWAVES, CAUSAL>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t e = set_smem_once(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
@@ -888,8 +887,7 @@ hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + (QB > 1 ? NWAVES * 4096 : 0) +
                           ((MODE & kModeBlockSparse) ? 2 * 2 * kBlockSparseMaxBlocks + 16 : 0);
   auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  hipError_t e = set_smem_once(kern, smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,

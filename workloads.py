@@ -33,8 +33,9 @@ def _randn(shape, gen, mult, dtype):
     return x.to(dtype)
 
 
-def prefill_inputs(B, N, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0, with_do=False, Nk=None):
-    """Q [B, N, Hq, d], K and V [B, Nk, Hkv, d] (and dO like Q), drawn in that order."""
+def prefill_inputs(B, N, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0, with_do=False, Nk=None, do_mult=1.0):
+    """Q [B, N, Hq, d], K and V [B, Nk, Hkv, d] (and dO like Q), drawn in that order.
+    ``mult`` scales Q, K and V; ``do_mult`` scales dO."""
     nk = N if Nk is None else Nk
     dt = DTYPES[dtype]
     gen = torch.Generator().manual_seed(seed)
@@ -43,7 +44,7 @@ def prefill_inputs(B, N, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0, with_do=Fal
     v = _randn((B, nk, Hkv, d), gen, mult, dt)
     out = {"q": q, "k": k, "v": v}
     if with_do:
-        out["do"] = _randn((B, N, Hq, d), gen, 1.0, dt)
+        out["do"] = _randn((B, N, Hq, d), gen, do_mult, dt)
     return out
 
 
