@@ -91,6 +91,7 @@ def assert_bf16_close(got, want, what: str):
 
 def assert_fp32_close(got, want, what: str):
     mx, mean = errors(got, want)
+    print(f"[parity] {what}: max {mx:.3e} mean {mean:.3e} (fp32)", flush=True)
     assert mx <= FP32_MAX_ABS, f"{what}: max {mx:.3e} mean {mean:.3e}"
     return mx, mean
 
