@@ -218,6 +218,34 @@ def fa_decode_kvcache(q, k_cache, v_cache, cache_seqlens, scale=None, causal=Fal
     return out, lse
 
 
+def fa_decode_kvcache_noalloc(q, k_cache, v_cache, cache_seqlens, out, lse=None, scale=None, num_splits=0):
+    """fa_decode_kvcache for callers that cannot allocate: no workspace is
+    allocated (the library's per-device scratch array holds the partials) and
+    the outputs are the caller's ``out`` [B, Hq, d] (and ``lse`` [B, Hq] or
+    None). Calls that overlap on one device race. Returns (out, lse)."""
+    _check_tensor("q", q, torch.bfloat16, 3)
+    dev = q.device
+    _check_tensor("k_cache", k_cache, torch.bfloat16, 4, dev)
+    _check_tensor("v_cache", v_cache, torch.bfloat16, 4, dev)
+    _check_tensor("cache_seqlens", cache_seqlens, torch.int32, 1, dev)
+    _check_tensor("out", out, torch.bfloat16, 3, dev)
+    B, Hq, d = q.shape
+    _, N, Hkv, _ = k_cache.shape
+    if (k_cache.shape != v_cache.shape or k_cache.shape[0] != B or k_cache.shape[3] != d
+            or cache_seqlens.shape[0] != B or out.shape != q.shape):
+        raise ValueError("inconsistent shapes for fa_decode_kvcache_noalloc")
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, 2, dev)
+        if tuple(lse.shape) != (B, Hq):
+            raise ValueError("lse must be [B, Hq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _lib.load().fa_decode_kvcache_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out),
+                                               _ptr(lse), B, Hq, Hkv, N, d, scale, 0, int(num_splits), _lib.FA_BF16,
+                                               _stream(dev))
+    _lib.check(st)
+    return out, lse
+
+
 def fa_decode_kvcache_ext(q, k_cache, v_cache, cache_seqlens, block_table=None, k_new=None, v_new=None, scale=None,
                           num_splits=0):
     """Decode with an optional in-place append (k_new, v_new: [B, Hkv, d]) and

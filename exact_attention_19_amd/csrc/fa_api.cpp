@@ -136,6 +136,43 @@ fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, co
   return hip_status(fn, all ? fa::launch_bwd(a, delta) : fa::launch_bwd_stage(a, delta, stage));
 }
 
+// Decode without append or paging. With use_scratch the partials go to the
+// library's per-device scratch array instead of the caller's workspace.
+fa_status decode_common(const char* fn, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_seqlens, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                        bool use_scratch, int B, int Hq, int Hkv, int N, int d, float scale, int num_splits,
+                        int dtype, void* stream) {
+  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
+  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
+  FA_TRY(check_ptr(fn, "q", q, 16));
+  FA_TRY(check_ptr(fn, "k_cache", k_cache, 16));
+  FA_TRY(check_ptr(fn, "v_cache", v_cache, 16));
+  FA_TRY(check_ptr(fn, "cache_seqlens", cache_seqlens, 4));
+  FA_TRY(check_ptr(fn, "o", o, 16));
+  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
+  const DecodePlan plan = decode_plan(B, Hq, Hkv, N, d, num_splits);
+  if (use_scratch) {
+    if (plan.bytes() > fa::kNoAllocScratchBytes)
+      return fail(FA_ERR_WORKSPACE, "%s: these sizes need %zu bytes of partials, more than the %zu-byte scratch "
+                  "array; use fa_decode_kvcache with a workspace", fn, plan.bytes(), fa::kNoAllocScratchBytes);
+    hipError_t e = hipSuccess;
+    workspace = fa::decode_noalloc_scratch(&e);
+    if (!workspace) return hip_status(fn, e);
+    workspace_bytes = fa::kNoAllocScratchBytes;
+  }
+  if (!workspace || workspace_bytes < plan.bytes())
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes(),
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
+  fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
+                   reinterpret_cast<hipStream_t>(stream)};
+  if (plan.P > 0) return hip_status(fn, fa::launch_decode_balanced(a, workspace, plan.P));
+  float* part_o = static_cast<float*>(workspace);
+  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes);
+  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, plan.chunk, plan.nsplit));
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,28 +318,16 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int N, int d, int num_s
 fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_cache, const int32_t* cache_seqlens,
                             void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                             int N, int d, float scale, int causal, int num_splits, int dtype, void* stream) {
-  static const char* fn = "fa_decode_kvcache";
+  return decode_common("fa_decode_kvcache", q, k_cache, v_cache, cache_seqlens, o, lse, workspace, workspace_bytes,
+                       false, B, Hq, Hkv, N, d, scale, num_splits, dtype, stream);
+}
+
+fa_status fa_decode_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                                    int d, float scale, int causal, int num_splits, int dtype, void* stream) {
   (void)causal;  // one query aligned to the bottom-right corner sees every cached key
-  FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
-  if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
-  if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "%s: num_splits must be >= 0", fn);
-  FA_TRY(check_ptr(fn, "q", q, 16));
-  FA_TRY(check_ptr(fn, "k_cache", k_cache, 16));
-  FA_TRY(check_ptr(fn, "v_cache", v_cache, 16));
-  FA_TRY(check_ptr(fn, "cache_seqlens", cache_seqlens, 4));
-  FA_TRY(check_ptr(fn, "o", o, 16));
-  if (lse && !aligned(lse, 4)) return fail(FA_ERR_INVALID_ARG, "%s: lse is not 4-byte aligned", fn);
-  const DecodePlan plan = decode_plan(B, Hq, Hkv, N, d, num_splits);
-  if (!workspace || workspace_bytes < plan.bytes())
-    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, plan.bytes(),
-                workspace ? workspace_bytes : (size_t)0);
-  if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
-  fa::DecodeArgs a{q, k_cache, v_cache, cache_seqlens, o, lse, B, Hq, Hkv, N, d, scale,
-                   reinterpret_cast<hipStream_t>(stream)};
-  if (plan.P > 0) return hip_status(fn, fa::launch_decode_balanced(a, workspace, plan.P));
-  float* part_o = static_cast<float*>(workspace);
-  float* part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.o_bytes);
-  return hip_status(fn, fa::launch_decode(a, part_o, part_lse, plan.chunk, plan.nsplit));
+  return decode_common("fa_decode_kvcache_noalloc", q, k_cache, v_cache, cache_seqlens, o, lse, nullptr, 0, true,
+                       B, Hq, Hkv, N, d, scale, num_splits, dtype, stream);
 }
 
 fa_status fa_decode_kvcache_ext(const void* q, void* k_cache, void* v_cache, const int32_t* cache_seqlens,

@@ -737,6 +737,13 @@ namespace {
 
 size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Partials of fa_decode_kvcache_noalloc: every call on a device shares this
+// array, so calls that overlap on one device race. Host code never passes
+// the array's name to a kernel (in host code it names a host-side stand-in);
+// it uses the address looked up per device below.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
 template <int D, int GP>
 const void* bal_kernel_ptr() {
   return reinterpret_cast<const void*>(decode_split_bal_kernel<D, GP, false>);
@@ -798,6 +805,25 @@ hipError_t launch_bal_gp(const DecodeArgs& a, int gp, void* ws, int P) {
 }
 
 }  // namespace
+
+void* decode_noalloc_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+    return nullptr;
+  }
+  g_scratch_addr[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
 
 int decode_balanced_ranges(int B, int Hq, int Hkv, int d, int num_splits) {
   if (num_splits != 0 || B > kDecBalMaxB || B <= 0 || (d != 64 && d != 128) || Hkv <= 0 || Hq % Hkv != 0) return 0;

@@ -156,4 +156,13 @@ struct DecodeBalLayout {
 DecodeBalLayout decode_bal_layout(int B, int Hq, int d, int P);
 hipError_t launch_decode_balanced(const DecodeArgs& a, void* workspace, int P);
 
+// The no-allocation decode entry point keeps its partials in a file-scope
+// device array of this many bytes (one copy per device, held until the
+// process ends).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// Device address of that array on the current device, looked up with
+// hipGetSymbolAddress on the first call on each device; nullptr (and *err
+// set) when the lookup fails.
+void* decode_noalloc_scratch(hipError_t* err);
+
 }  // namespace fa

@@ -227,6 +227,30 @@ fa_status fa_decode_kvcache(const void* q, const void* k_cache, const void* v_ca
                             int num_splits, int dtype, void* stream);
 
 /*
+ * fa_decode_kvcache without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and errors as
+ * fa_decode_kvcache, whose kernels it launches; the split partials go to a
+ * file-scope device array of FA_NOALLOC_SCRATCH_BYTES (64 MiB) that each
+ * device the library runs on holds until the process ends. The call itself
+ * allocates and frees nothing; its first call on a device looks up the
+ * array's address there.
+ *   Sizes whose partials exceed the array (fa_decode_workspace_bytes(...,
+ *   num_splits) > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE before any
+ *   launch; the 64-sequence, Hq=32, Hkv=8, d=128, 32k-row cache decode needs
+ *   about a sixth of it.
+ * Every call on one device shares that device's array, and the array keeps
+ * the last call's contents (nothing in it needs to start at zero): calls
+ * that overlap on one device, on different streams or threads, race.
+ * Serialise them (one stream, or synchronise between calls).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fa_status fa_decode_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, void* o, float* lse,
+                                    int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                                    int num_splits, int dtype, void* stream);
+
+/*
  * Decode with an in-place cache append and/or a paged KV cache
  * (flash_attn_with_kvcache updates k_cache/v_cache in place: hysenlabs
  * digest, outputs section; paged KV cache: v2.5 entry of the changelog in

@@ -210,3 +210,16 @@ def test_error_message_is_per_call(lib):
     assert _fwd(lib, B=0) == _lib.FA_ERR_INVALID_ARG
     assert "sizes" in lib.fa_last_error().decode()
     assert isinstance(lib.fa_version(), bytes) and ctypes.sizeof(ctypes.c_size_t) == 8
+
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch(lib):
+    """Partials larger than the 64 MiB scratch array: FA_ERR_WORKSPACE before
+    any HIP call (an explicit split count plans without querying a device)."""
+    B, Hq, Hkv, N, d, ns = 512, 64, 8, 65536, 128, 64
+    assert lib.fa_decode_workspace_bytes(B, Hq, Hkv, N, d, ns) > (64 << 20)
+    st = lib.fa_decode_kvcache_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, None, B, Hq, Hkv, N, d, 0.1, 0, ns,
+                                       _lib.FA_BF16, None)
+    assert st == _lib.FA_ERR_WORKSPACE
+    assert lib.fa_last_error().decode().startswith("fa_decode_kvcache_noalloc")
+    assert lib.fa_decode_kvcache_noalloc(None, FAKE, FAKE, FAKE, FAKE, None, 2, 4, 2, 64, 128, 0.1, 0, 0,
+                                         _lib.FA_BF16, None) == _lib.FA_ERR_INVALID_ARG
