@@ -344,6 +344,10 @@ def extras(fa_mod, lib, dev):
     tf_ = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=True, out=o, lse=lse))
     tb_ = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True))
     ms_f, ms_b = tf_["ms"], tb_["ms"]
+    ta_ = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True, deterministic=False))
+    out["gqa_bwd_atomic"] = {"workload": f"B={B} N={N} Hq={H} Hkv={Hkv} d={d} causal", **ta_,
+                             "TFLOP/s": round(2.5 * 4 * d * pairs / (ta_["ms"] * 1e9), 1),
+                             "note": "fa_bwd_atomic: preprocess + fused dK/dV/dQ (fp32 atomic dQ) + dQ convert"}
     out["gqa_fwd_bwd"] = {"workload": f"B={B} N={N} Hq={H} Hkv={Hkv} d={d} causal", "fwd": tf_, "bwd": tb_,
                           "fwd_TFLOP/s": round(4 * d * pairs / (ms_f * 1e9), 1),
                           "fwd+bwd TFLOP/s": round(3.5 * 4 * d * pairs / ((ms_f + ms_b) * 1e9), 1),
@@ -360,6 +364,14 @@ def extras(fa_mod, lib, dev):
     tf_ = _time_ms(lambda: fa_mod.fa_fwd_window(q, k, v, (wl, 0), causal=True, out=o, lse=lse))
     tb_ = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True, window=(wl, 0)))
     ms_f, ms_b = tf_["ms"], tb_["ms"]
+    o_full, lse_full = fa_mod.fa_fwd(q, k, v, causal=True)
+    ta_ = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o_full, do, lse_full, causal=True, deterministic=False))
+    pairs_full = _pairs_band(N, N, True) * B * H
+    out["bwd_atomic"] = {"workload": f"B={B} N={N} H={H} d={d} causal", **ta_,
+                         "TFLOP/s": round(2.5 * 4 * d * pairs_full / (ta_["ms"] * 1e9), 1),
+                         "note": "fa_bwd_atomic: preprocess + fused dK/dV/dQ (fp32 atomic dQ) + dQ convert; "
+                                 "compare kernels.bwd_* (deterministic)"}
+    del o_full, lse_full
     out["window_fwd"] = {"workload": f"B={B} N={N} H={H} d={d} causal window (4095, 0)", **tf_,
                          "TFLOP/s": round(4 * d * pairs / (ms_f * 1e9), 1)}
     out["window_bwd"] = {"workload": out["window_fwd"]["workload"], **tb_,

@@ -40,6 +40,10 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_bwd_atomic_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "fa_bwd_atomic": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_bwd_atomic_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I,
+                                 _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I, _I]),
     "fa_decode_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _SZ, _I, _I, _I, _I, _I, _F, _I, _I, _I, _P]),

@@ -150,10 +150,12 @@ def fa_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False):
     return out, lse
 
 
-def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=None, dk=None, dv=None):
+def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=None, dk=None, dv=None,
+           deterministic=True):
     """Attention backward from the forward's O and LSE. Returns (dq, dk, dv),
     written into the given tensors when passed. A window other than (-1, -1)
-    calls fa_bwd_window (d = 128)."""
+    calls fa_bwd_window (d = 128); deterministic=False calls fa_bwd_atomic
+    (d = 128, no window: dQ accumulated with fp32 atomics)."""
     _check_tensor("q", q, torch.bfloat16, 4)
     dev = q.device
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -165,7 +167,11 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=
         raise ValueError("inconsistent shapes for fa_bwd")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = _lib.load()
-    ws_bytes = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, d)
+    wl, wr = (int(x) for x in window)
+    atomic = not deterministic
+    if atomic and (wl >= 0 or wr >= 0):
+        raise ValueError("the atomic backward has no window")
+    ws_bytes = (lib.fa_bwd_atomic_workspace_bytes if atomic else lib.fa_bwd_workspace_bytes)(B, Hq, Hkv, N, d)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -175,8 +181,11 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=
     _check_tensor("dv", dv, torch.bfloat16, 4, dev)
     if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
         raise ValueError("dq/dk/dv must have the shapes of q/k/v")
-    wl, wr = (int(x) for x in window)
-    if wl < 0 and wr < 0:
+    if atomic:
+        st = lib.fa_bwd_atomic(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16,
+                               _stream(dev))
+    elif wl < 0 and wr < 0:
         st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                         _ptr(ws), ws_bytes, B, Hq, Hkv, N, d, scale, int(bool(causal)), _lib.FA_BF16, _stream(dev))
     else:

@@ -100,9 +100,10 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int N, int d, int num_splits) {
 fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, const void* v, const void* o,
                      const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                     int dtype, void* stream, int window_left = -1, int window_right = -1) {
+                     int dtype, void* stream, int window_left = -1, int window_right = -1, bool atomic = false) {
   FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
   if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is implemented (dtype %d)", fn, dtype);
+  if (atomic && d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: the atomic backward needs d = 128 (got %d)", fn, d);
   if (window_left < -1 || window_right < -1)
     return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
   if ((window_left >= 0 || window_right >= 0) && d != 128)
@@ -125,13 +126,14 @@ fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, co
     FA_TRY(check_ptr(fn, "dv", dv, 16));
   }
   if (all || stage == 2) FA_TRY(check_ptr(fn, "dq", dq, 16));
-  const size_t need = bwd_ws_bytes(B, Hq, N);
+  const size_t need = atomic ? fa::bwd_atomic_ws_bytes(B, Hq, N, d) : bwd_ws_bytes(B, Hq, N);
   if (!workspace || workspace_bytes < need)
     return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 256)) return fail(FA_ERR_INVALID_ARG, "%s: workspace is not 256-byte aligned", fn);
   fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, N, d, scale, causal ? 1 : 0,
                 reinterpret_cast<hipStream_t>(stream), window_left, window_right};
+  if (atomic) a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + fa::bwd_atomic_acc_offset(B, Hq, N));
   float* delta = static_cast<float*>(workspace);
   return hip_status(fn, all ? fa::launch_bwd(a, delta) : fa::launch_bwd_stage(a, delta, stage));
 }
@@ -300,6 +302,29 @@ fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, c
   if (stage < 0 || stage > 2) return fail(FA_ERR_INVALID_ARG, "fa_bwd_stage: stage %d is not 0, 1 or 2", stage);
   return bwd_common("fa_bwd_stage", stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq,
                     Hkv, N, d, scale, causal, dtype, stream);
+}
+
+size_t fa_bwd_atomic_workspace_bytes(int B, int Hq, int Hkv, int N, int d) {
+  (void)Hkv;
+  if (B <= 0 || Hq <= 0 || N <= 0 || d <= 0) return 0;
+  return fa::bwd_atomic_ws_bytes(B, Hq, N, d);
+}
+
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream) {
+  return bwd_common("fa_bwd_atomic", -1, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv,
+                    N, d, scale, causal, dtype, stream, -1, -1, true);
+}
+
+fa_status fa_bwd_atomic_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                              int dtype, void* stream) {
+  if (stage < 0 || stage > 2)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd_atomic_stage: stage %d is not 0, 1 or 2", stage);
+  return bwd_common("fa_bwd_atomic_stage", stage, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B,
+                    Hq, Hkv, N, d, scale, causal, dtype, stream, -1, -1, true);
 }
 
 fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
                                                              const __bf16* __restrict__ dout,
                                                              const float* __restrict__ lse,
                                                              float* __restrict__ delta, float* __restrict__ lse2,
-                                                             int B, int Hq, int N) {
+                                                             int B, int Hq, int N, float* __restrict__ dq_acc) {
   constexpr int LPT = D / 8;
   const int64_t rows = (int64_t)B * N * Hq;
   const int64_t gt = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -63,6 +63,11 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
   const int dl = (int)(gt % LPT);
   const bool ok = r < rows;
   const int64_t rr = ok ? r : 0;
+  if (dq_acc && ok) {  // the atomic backward's fp32 dQ accumulator starts at zero
+    f32x4* z = reinterpret_cast<f32x4*>(dq_acc + rr * D + dl * 8);
+    z[0] = f32x4{};
+    z[1] = f32x4{};
+  }
   const u32x4 a = *reinterpret_cast<const u32x4*>(o + rr * D + dl * 8);
   const u32x4 g = *reinterpret_cast<const u32x4*>(dout + rr * D + dl * 8);
   const float tot = row_group_sum<LPT>(dot8_bf16(a, g, 0.f));
@@ -76,6 +81,21 @@ __global__ __launch_bounds__(256) void bwd_preprocess_kernel(const __bf16* __res
     delta[idx] = tot;
     lse2[idx] = lse[idx] * kLog2e;  // exponent reference in log2 units
   }
+}
+
+// dQ = bf16(scale * dQacc), 8 elements per thread (the atomic backward).
+__global__ __launch_bounds__(256) void bwd_dq_finalize_kernel(const float* __restrict__ acc, __bf16* __restrict__ dq,
+                                                              int64_t n8, float scale) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4* a = reinterpret_cast<const f32x4*>(acc + 8 * i);
+  const f32x4 x = a[0], y = a[1];
+  u32x4 w;
+  w[0] = pack_bf16x2(x[0] * scale, x[1] * scale);
+  w[1] = pack_bf16x2(x[2] * scale, x[3] * scale);
+  w[2] = pack_bf16x2(y[0] * scale, y[1] * scale);
+  w[3] = pack_bf16x2(y[2] * scale, y[3] * scale);
+  *reinterpret_cast<u32x4*>(dq + 8 * i) = w;
 }
 
 // ---------------------------------------------------------------------------
@@ -499,15 +519,24 @@ __device__ __forceinline__ int row_offset(int lane) {
 // keys k0 + 32w .. +31 (K, V fragments and dK^T, dV^T accumulators in
 // registers) and sweeps the visible 64-row query tiles of every query head
 // in the GQA group.
-template <bool CAUSAL, bool WINDOW, int BQ>
+//
+// FUSED (the atomic backward) also produces dQ, so that the backward runs
+// the five N x N x d products once each instead of recomputing S and dP in a
+// separate dQ kernel: every wave writes its dS block to an LDS tile
+// [64 queries x 128 keys], and during the next step wave w adds
+// dQ[:, 32w .. 32w+31] += dS K over the workgroup's 128 keys (K kept in LDS)
+// into an fp32 accumulator with atomic adds (so dQ's last bits depend on the
+// order in which workgroups arrive).
+template <bool CAUSAL, bool WINDOW, int BQ, bool FUSED = false>
 __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
-    float scale_log2, int win_left, int win_right) {
+    float scale_log2, int win_left, int win_right, float* __restrict__ dq_acc) {
   constexpr int D = 128, DS = 8, DB = 4, BKV = 128;
   constexpr int NQB = BQ / 32;                 // 32-query blocks per query tile
   static_assert(BQ == 64 || BQ == 128, "query tiles of 64 or 128 rows");
+  static_assert(!FUSED || (BQ == 64 && !WINDOW), "fused dQ: 64-query tiles, no window");
   // Key j is visible to query i iff j <= i (causal), i - wl <= j <= i + wr
   // (window, a negative side unbounded) and both are < N.
   const int wl = WINDOW ? win_left : -1;
@@ -515,6 +544,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   constexpr int TILE = BQ * 256;               // one BQ x 128 bf16 tile (Q, then dO)
   constexpr int VEC_OFF = 2 * TILE;            // lse2 (BQ floats) then delta (BQ floats)
   constexpr int STAGE = 2 * TILE + 8 * BQ;
+  constexpr int KT_OFF = 2 * STAGE;            // FUSED: the workgroup's 128 K rows (two 64-row tiles)
+  constexpr int DSB_OFF = KT_OFF + 2 * 16384;  // FUSED: two [64 x 128] dS tiles, by step parity
   extern __shared__ __align__(1024) unsigned char smem[];
 
   const int lane = threadIdx.x & 63;
@@ -693,11 +724,68 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
       }
     }
   };
+  // FUSED: dS of block qb into the LDS tile dsb, row = query within the tile,
+  // 16-byte units swizzled as the Q tiles. Within each 16-key group, keys
+  // 4-7 and 8-11 trade places (bits 2 and 3 of the key swapped), so that one
+  // 16-byte row read yields keys {0-3, 8-11} (lanes 0-31) or {4-7, 12-15}
+  // (lanes 32-63): the order in which the transposed K operand pairs them.
+  // A key past N (its K row, loaded clamped, stands in for the last key) gets
+  // dS = 0 here, so it adds nothing to dQ whatever its scores were.
+  auto store_ds = [&](unsigned char* dsb, int qb, const Probs& pr) __attribute__((always_inline)) {
+    const int kl = 32 * wave + l32;
+    const int pos = (kl & ~15) | (kl & 3) | ((kl & 4) << 1) | ((kl & 8) >> 1);
+    const int unit = pos >> 3, byte = 2 * (pos & 7);
+    const bool valid = my_key < N;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = 32 * qb + 8 * (e >> 2) + 4 * hh + (e & 3);
+      *reinterpret_cast<__bf16*>(dsb + row * 256 + 16 * (unit ^ tile_swz(row)) + byte) =
+          valid ? pr.ds[e >> 3][e & 7] : (__bf16)0.f;
+    }
+  };
+  // FUSED: dQ rows q0 .. q0+63, columns 32w .. 32w+31 of query head hq from
+  // the dS tile of that step: 16 MFMAs over the 128 keys (16-key steps of
+  // waves whose keys the tile skipped are left out), then one atomic add per
+  // element.
+  auto dq_pass = [&](const unsigned char* dsb, int hq, int q0, int skipmask) __attribute__((always_inline)) {
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (skipmask & (1 << (ks >> 1))) continue;
+      const bf16x8 kop = tr_operand(smem + KT_OFF, ks, wave, toff);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        acc[qb] = mfma32(*reinterpret_cast<const bf16x8*>(dsb + qb * 8192 + (roff ^ (32 * ks))), kop, acc[qb]);
+    }
+    if (skipmask == 15) return;
+    float* base = dq_acc + ((int64_t)b * N + q0) * q_rs + (int64_t)hq * D + 32 * wave + l32;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * qb + 8 * (e >> 2) + 4 * hh + (e & 3);
+        if (q0 + row < N) unsafeAtomicAdd(base + (int64_t)row * q_rs, acc[qb][e]);
+      }
+    }
+  };
+  // Waves whose 32 keys see no query of the tile at q0 (bit w set).
+  auto skip_mask = [&](int q0) __attribute__((always_inline)) {
+    int m = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int kw = k0 + 32 * w;
+      if (kw >= N || (CAUSAL && q0 + BQ - 1 < kw)) m |= 1 << w;
+    }
+    return m;
+  };
+  int prev_hq = 0, prev_q0 = 0, prev_skip = 15;
+
   // MASK is a compile-time tag: tiles without masking (all but the causal
   // diagonal and the ragged end) run a branch-free body, one scheduling
   // region. (Pinning its issue order as in the dQ kernel measured slower
   // here, with one wave per SIMD; the compiler's order is kept.)
-  auto tile_body = [&](const unsigned char* st, int q0, auto mask_tag) __attribute__((always_inline)) {
+  auto tile_body = [&](const unsigned char* st, int q0, auto mask_tag, unsigned char* dsb)
+                       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // Skewed over the NQB blocks: the scores of block qb + 1 are issued
     // before the algebra and products of block qb.
@@ -712,6 +800,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
         if constexpr (MASK) apply_mask(sb, q0, qb + 1);
       }
       update(st, qb, p);
+      if constexpr (FUSED) store_ds(dsb, qb, p);
       if (qb + 1 < NQB) sa = sb;
     }
   };
@@ -719,14 +808,25 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   auto step = [&](int it, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
     constexpr int STG = decltype(stage_tag)::value;
     const Cursor nxt = advance(it, cur);
+    // FUSED: dQ of the previous step (its dS tile completed at the barrier
+    // that ended it); the atomics go out before this step's DMA, and the
+    // wait below covers both.
+    if constexpr (FUSED) {
+      if (it > 0) dq_pass(smem + DSB_OFF + (STG ^ 1) * 16384, prev_hq, prev_q0, prev_skip);
+    }
     if (it + 1 < n_iter) issue(it + 1, nxt, STG ^ 1);
-    int hq_unused, q0;
-    tile_at(it, cur, hq_unused, q0);
+    int hq_cur, q0;
+    tile_at(it, cur, hq_cur, q0);
     cur = nxt;
     bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
     if (WINDOW && wr >= 0) skip = skip || q0 + BQ - 1 < kw0 - wr;
     if (WINDOW && wl >= 0) skip = skip || q0 > kw0 + 31 + wl;
-    if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag);
+    if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag, smem + DSB_OFF + STG * 16384);
+    if constexpr (FUSED) {
+      prev_hq = hq_cur;
+      prev_q0 = q0;
+      prev_skip = skip_mask(q0);
+    }
     wait_vmcnt<0>();
     barrier_keep_dma();
   };
@@ -734,6 +834,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   using S1 = std::integral_constant<int, 1>;
 
   if (n_iter > 0) issue(0, cur, 0);
+  if constexpr (FUSED) {
+    const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+    const uint32_t kdma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
+    const unsigned char* kt = reinterpret_cast<const unsigned char*>(k) + ((int64_t)b * N + k0) * kv_rs * 2 +
+                              (int64_t)hk * D * 2;
+    dma_rows64(kt, kv_rs_bytes, N - k0, smem + KT_OFF, wave, 4, 4, kdma_off);
+    dma_rows64(kt + (int64_t)64 * kv_rs * 2, kv_rs_bytes, N - k0 - 64, smem + KT_OFF + 16384, wave, 4, 4, kdma_off);
+  }
   wait_vmcnt<0>();
   barrier_keep_dma();
   int it = 0;
@@ -747,6 +855,9 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     step(it + 1, S1{}, std::false_type{});
   }
   if (it < n_iter) step(it, S0{}, std::false_type{});
+  if constexpr (FUSED) {
+    if (n_iter > 0) dq_pass(smem + DSB_OFF + ((n_iter - 1) & 1) * 16384, prev_hq, prev_q0, prev_skip);
+  }
 
   if (!wave_active || my_key >= N) return;
   const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
@@ -1028,13 +1139,26 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
     const int64_t grid = (threads + 255) / 256;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(bwd_preprocess_kernel<D>, dim3((unsigned)grid), dim3(256), 0, a.stream,
-                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, delta, lse2, a.B, a.Hq, a.N);
+                       (const __bf16*)a.o, (const __bf16*)a.dout, a.lse, delta, lse2, a.B, a.Hq, a.N, a.dq_acc);
     return hipGetLastError();
   }
   if (stage == 1) {
     const int nkt = (a.N + 127) / 128;
     const int64_t grid = (int64_t)nkt * a.B * a.Hkv;
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if constexpr (D == 128 && !WINDOW) {
+      if (a.dq_acc) {
+        auto kern = bwd_dkdv_d128_kernel<CAUSAL, false, 64, true>;
+        constexpr size_t smem = 2 * (2 * 64 * 256 + 8 * 64) + 2 * 16384 + 2 * 16384;
+        hipError_t e = set_smem_once(kern, smem);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
+                           (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
+                           (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
+                           scale_log2, -1, -1, a.dq_acc);
+        return hipGetLastError();
+      }
+    }
     if (D == 128) {
       constexpr int BQ = kDkdvQueryTile;
       auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>;
@@ -1044,7 +1168,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
                          (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
-                         scale_log2, a.win_left, a.win_right);
+                         scale_log2, a.win_left, a.win_right, nullptr);
       return hipGetLastError();
     }
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
@@ -1054,6 +1178,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
                        (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
                        scale_log2);
+    return hipGetLastError();
+  }
+  if (a.dq_acc) {  // atomic backward: dQ = bf16(scale * dQacc)
+    const int64_t n8 = (int64_t)a.B * a.N * a.Hq * D / 8;
+    const int64_t grid = (n8 + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(bwd_dq_finalize_kernel, dim3((unsigned)grid), dim3(256), 0, a.stream, (const float*)a.dq_acc,
+                       (__bf16*)a.dq, n8, a.scale);
     return hipGetLastError();
   }
   const int nqt = (a.N + 127) / 128;

@@ -90,6 +90,10 @@ struct BwdArgs {
   hipStream_t stream;
   int win_left = -1;   // sliding window (d = 128 only); -1 = unbounded side
   int win_right = -1;
+  // Atomic backward (d = 128, no window): fp32 dQ accumulator [B, N, Hq, d];
+  // stage 0 also zeroes it, stage 1 is the fused dK/dV/dQ kernel, stage 2
+  // converts it to dq. NULL: the deterministic three-kernel backward.
+  float* dq_acc = nullptr;
 };
 
 struct DecodeArgs {
@@ -137,6 +141,12 @@ hipError_t launch_fwd_blocksparse(const FwdArgs& a, const FwdSeq& seq);
 // Stage 0 computes both, stage 1 dK and dV, stage 2 dQ; launch_bwd runs all three.
 inline size_t bwd_vec_stride(int B, int Hq, int N) {
   return ((size_t)B * Hq * N + 63) / 64 * 64;  // floats; keeps the second vector 256-byte aligned
+}
+// Atomic backward workspace: the two vectors above, then the fp32 dQ
+// accumulator (256-byte aligned).
+inline size_t bwd_atomic_acc_offset(int B, int Hq, int N) { return 2 * bwd_vec_stride(B, Hq, N) * sizeof(float); }
+inline size_t bwd_atomic_ws_bytes(int B, int Hq, int N, int d) {
+  return bwd_atomic_acc_offset(B, Hq, N) + (size_t)B * N * Hq * d * sizeof(float);
 }
 hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage);
 hipError_t launch_bwd(const BwdArgs& a, float* delta);

@@ -190,6 +190,38 @@ fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void*
                         size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, float scale,
                         int causal, int window_left, int window_right, int dtype, void* stream);
 
+/*
+ * Non-deterministic backward with the same inputs, outputs and layouts as
+ * fa_bwd: one fused kernel per (batch, kv head, 128 keys) computes dK and
+ * dV as fa_bwd does and also dQ, which it accumulates in fp32 with atomic
+ * adds (the recompute backward of the abeam summary, "学習時の backward では
+ * 再計算を使う", with the S and dP products done once for all three
+ * gradients). The flash-attention API takes a `deterministic` flag and its
+ * changelog adds the deterministic backward in v2.4 (hysenlabs digest,
+ * "出力と運用記録" and "制約を切り分ける確認"); here fa_bwd is that
+ * deterministic backward and this is the other one. dK and dV are bitwise
+ * equal to fa_bwd's; dQ may differ from run to run in its last bits (the
+ * order of the fp32 additions).
+ *   workspace: at least fa_bwd_atomic_workspace_bytes(...) bytes (D and
+ *   LSE*log2(e) as for fa_bwd, then a [B,N,Hq,d] float32 dQ accumulator),
+ *   256-byte aligned.
+ * d = 128, bf16 only (FA_ERR_UNSUPPORTED otherwise); errors as fa_bwd.
+ */
+size_t fa_bwd_atomic_workspace_bytes(int B, int Hq, int Hkv, int N, int d);
+fa_status fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                        int dtype, void* stream);
+/* fa_bwd_atomic one launch at a time (for timing): stage 0 computes D and
+ * LSE*log2(e) and zeroes the dQ accumulator, stage 1 runs the fused kernel,
+ * stage 2 writes dq from the accumulator. */
+fa_status fa_bwd_atomic_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                              const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                              int dtype, void* stream);
+
 /* Bytes of device workspace fa_decode_kvcache needs (num_splits as passed to it).
  * With num_splits = 0 the size depends on the current device (the balanced
  * split described below sizes its partials by the device's resident

@@ -77,3 +77,38 @@ def test_bwd_deterministic():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+ATOMIC = [
+    # B, N, Hq, Hkv, d (d = 128 only)
+    (1, 1, 1, 1, 128),
+    (1, 64, 2, 2, 128),
+    (2, 130, 4, 2, 128),
+    (1, 257, 8, 2, 128),
+    (1, 300, 16, 2, 128),
+    (1, 512, 2, 1, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", ATOMIC, ids=[f"B{b}N{n}Hq{hq}Hkv{hk}d{d}" for b, n, hq, hk, d in ATOMIC])
+def test_bwd_atomic(shape, causal):
+    """fa_bwd_atomic: dQ, dK, dV against the oracle; dK and dV bitwise equal
+    to the deterministic backward's; every output written (NaN-filled)."""
+    fa = need_gpu()
+    B, N, Hq, Hkv, d = shape
+    announce(f"bwd atomic {shape} causal={causal}")
+    dev = torch.device("cuda:0")
+    inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=300 + N, with_do=True)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fa_fwd(q, k, v, causal=causal)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    fa.fa_bwd(q, k, v, o, do, lse, causal=causal, dq=dq, dk=dk, dv=dv, deterministic=False)
+    rq, rk, rv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dk, rk) and torch.equal(dv, rv)
+    rdq, rdk, rdv, _ = oracle.attn_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]),
+                                       1 / math.sqrt(d), causal)
+    assert_bf16_close(dq, rdq, "dQ")
+    assert_bf16_close(dk, rdk, "dK")
+    assert_bf16_close(dv, rdv, "dV")
