@@ -573,6 +573,10 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
       if (__builtin_amdgcn_ballot_w64(!(p0[j].sum <= kSumLimit))) p0[j] = resync(j, s0.s[j]);
       l_run[j] += p0[j].sum;
     }
+    // Issue priority while this wave feeds its P V MFMAs: when both waves of
+    // a SIMD are ready, the one holding the matrix pipe keeps it (measured
+    // 0.5-5 % faster, bitwise equal).
+    __builtin_amdgcn_s_setprio(1);
     pv(vs, 0, p0);
 #pragma unroll
     for (int j = 0; j < QB; ++j) p1[j] = probs(s1.s[j], -m_run[j]);
@@ -593,6 +597,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
       l_run[j] += p1[j].sum;
     }
     pv(vs, 1, p1);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Tiles are prefetched NSTAGE - 1 ahead into a ring of LDS stages. Step t
