@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads of the oracle sample")
     ap.add_argument("--no-decode", action="store_true", help="leave the decode stage out (profiling only)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock/power reading (profiling runs: it starts a child process and "
+                         "adds steps outside the timed region)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary measurements (window, varlen, paged decode, block-sparse)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -522,7 +525,7 @@ def main():
 
     # Clock and power under this load: the step back to back for a few
     # seconds while amd-smi is read (outside the timed region).
-    clock = sustained_clock(lambda: [fn() for _, fn in stages], 4.0)
+    clock = None if args.no_clock else sustained_clock(lambda: [fn() for _, fn in stages], 4.0)
 
     fwd_flops = w.fwd_flops()
     bwd_flops = w.bwd_flops()
