@@ -58,6 +58,8 @@ SWEEP = [
     (1, 1000, 4, 1, 128),
     (1, 333, 16, 2, 64),
     (1, 2113, 2, 1, 128),
+    (1, 2113, 2, 1, 64),     # d = 64, key range split over the waves, 17 steps of 128 keys
+    (4, 1100, 16, 4, 64),    # d = 64 with 576 workgroups of 128 rows: the unsplit kernel
 ]
 
 
