@@ -342,9 +342,14 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
 
   // Register staging of one step (two tiles); rows past N read row N - 1
   // (their scores are masked, so the duplicates never count).
+  // Every thread issues the same number of loads (two K chunks of each tile,
+  // one V group of the step), so the compiler can wait for one step's loads
+  // while the next step's are in flight.
+  static_assert(2 * V_GROUPS == NT, "one V group of the step per thread");
+  const int v_ti = tid / V_GROUPS, v_g = tid % V_GROUPS;
   u32x4 kA[2][K_PER_T], kB[2][K_PER_T];
-  u32x4 vA[2][4], vB[2][4];
-  auto load_step = [&](int st, u32x4 (&kr)[2][K_PER_T], u32x4 (&vr)[2][4]) __attribute__((always_inline)) {
+  u32x4 vA[4], vB[4];
+  auto load_step = [&](int st, u32x4 (&kr)[2][K_PER_T], u32x4 (&vr)[4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
       const int k0 = st * 128 + ti * kBN;
@@ -354,15 +359,13 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
         const int row = c / C8, col = c % C8;
         kr[ti][r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)min(k0 + row, N - 1) * kv_rs + col * 8);
       }
-      if (tid < V_GROUPS) {
-        const int dc = tid % C8, kg = tid / C8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vr[ti][i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)min(k0 + kg * 4 + i, N - 1) * kv_rs + dc * 8);
-      }
     }
+    const int k0 = st * 128 + v_ti * kBN + (v_g / C8) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)min(k0 + i, N - 1) * kv_rs + (v_g % C8) * 8);
   };
-  auto store_step = [&](int stage, const u32x4 (&kr)[2][K_PER_T], const u32x4 (&vr)[2][4])
+  auto store_step = [&](int stage, const u32x4 (&kr)[2][K_PER_T], const u32x4 (&vr)[4])
                         __attribute__((always_inline)) {
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti) {
@@ -372,8 +375,8 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
         const int c = tid + r * NT;
         *reinterpret_cast<u32x4*>(ks + (c / C8) * SM::KS + (c % C8) * 8) = kr[ti][r];
       }
-      if (tid < V_GROUPS) store_transposed_4x8(ks + SM::K_ELEMS, tid / C8, tid % C8, vr[ti]);
     }
+    store_transposed_4x8(smem + stage * STEP_ELEMS + v_ti * TILE_ELEMS + SM::K_ELEMS, v_g / C8, v_g % C8, vr);
   };
 
   f32x16 oacc[DB];
@@ -433,17 +436,20 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
     }
   };
 
+  // The loads run two steps ahead and are issued unconditionally (past the
+  // last step they read clamped rows that are never stored): with the same
+  // loads on every path, the wait before a store covers only the older step.
   load_step(0, kA, vA);
-  if (n_steps > 1) load_step(1, kB, vB);
+  load_step(1, kB, vB);
   store_step(0, kA, vA);
   __syncthreads();
   for (int st = 0; st < n_steps; st += 2) {
-    if (st + 2 < n_steps) load_step(st + 2, kA, vA);
+    load_step(st + 2, kA, vA);
     compute(st);
     if (st + 1 < n_steps) store_step(1, kB, vB);
     __syncthreads();
     if (st + 1 >= n_steps) break;
-    if (st + 3 < n_steps) load_step(st + 3, kB, vB);
+    load_step(st + 3, kB, vB);
     compute(st + 1);
     if (st + 2 < n_steps) store_step(0, kA, vA);
     __syncthreads();
