@@ -1150,7 +1150,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       if (a.dq_acc) {
         auto kern = bwd_dkdv_d128_kernel<CAUSAL, false, 64, true>;
         constexpr size_t smem = 2 * (2 * 64 * 256 + 8 * 64) + 2 * 16384 + 2 * 16384;
-        hipError_t e = set_smem_once(kern, smem);
+        hipError_t e = set_smem_once<bwd_dkdv_d128_kernel<CAUSAL, false, 64, true>>(smem);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                            (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1163,7 +1163,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       constexpr int BQ = kDkdvQueryTile;
       auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>;
       constexpr size_t smem = 2 * (2 * BQ * 256 + 8 * BQ);
-      hipError_t e = set_smem_once(kern, smem);
+      hipError_t e = set_smem_once<bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>>(smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1172,7 +1172,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
       return hipGetLastError();
     }
     auto kern = bwd_dkdv_kernel<D, CAUSAL>;
-    hipError_t e = set_smem_once(kern, DkdvSmem<D>::BYTES);
+    hipError_t e = set_smem_once<bwd_dkdv_kernel<D, CAUSAL>>(DkdvSmem<D>::BYTES);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DkdvSmem<D>::BYTES, a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
@@ -1194,7 +1194,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   if (D == 128) {
     auto kern = bwd_dq_d128_kernel<CAUSAL, WINDOW>;
     constexpr size_t smem = 2 * 2 * 64 * 256;
-    hipError_t e = set_smem_once(kern, smem);
+    hipError_t e = set_smem_once<bwd_dq_d128_kernel<CAUSAL, WINDOW>>(smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1203,7 +1203,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
     return hipGetLastError();
   }
   auto kern = bwd_dq_kernel<D, CAUSAL>;
-  hipError_t e = set_smem_once(kern, DqSmem<D>::BYTES);
+  hipError_t e = set_smem_once<bwd_dq_kernel<D, CAUSAL>>(DqSmem<D>::BYTES);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,

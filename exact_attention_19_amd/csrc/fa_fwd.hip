@@ -1105,7 +1105,7 @@ hipError_t launch_bf16(const FwdArgs& a) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   const size_t smem = FwdSmem<D, NWAVES>::BYTES;
   auto kern = fwd_bf16_kernel<D, NWAVES, CAUSAL>;
-  hipError_t e = set_smem_once(kern, smem);
+  hipError_t e = set_smem_once<fwd_bf16_kernel<D, NWAVES, CAUSAL>>(smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
@@ -1125,7 +1125,7 @@ hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + (QB > 1 ? NWAVES * 4096 : 0) +
                           ((MODE & kModeBlockSparse) ? 2 * 2 * kBlockSparseMaxBlocks + 16 : 0);
   auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>;
-  hipError_t e = set_smem_once(kern, smem);
+  hipError_t e = set_smem_once<fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>>(smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
@@ -1140,7 +1140,7 @@ hipError_t launch_splitk64(const FwdArgs& a) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   constexpr size_t smem = 2 * 2 * FwdSmem<64, 4>::STAGE_ELEMS * 2;
   auto kern = fwd_splitk_d64_kernel<CAUSAL>;
-  hipError_t e = set_smem_once(kern, smem);
+  hipError_t e = set_smem_once<fwd_splitk_d64_kernel<CAUSAL>>(smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), smem, a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles);

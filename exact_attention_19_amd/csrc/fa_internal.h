@@ -15,16 +15,18 @@ constexpr int kMaxDevices = 64;
 
 // Raises a kernel's dynamic-LDS limit once per device, on the first launch
 // there: one flag per kernel and device (the library's only state besides the
-// thread-local error text and the per-device values named above). Racing
-// first calls may both set the attribute, which is harmless.
-template <typename K>
-hipError_t set_smem_once(K kern, size_t bytes) {
+// thread-local error text and the per-device values named above). The kernel
+// is a template argument, so every kernel instantiation has flags of its own
+// (kernels that differ only in template arguments share a function-pointer
+// type). Racing first calls may both set the attribute, which is harmless.
+template <auto KERN>
+hipError_t set_smem_once(size_t bytes) {
   static std::atomic<unsigned char> done[kMaxDevices];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev >= 0 && dev < kMaxDevices && done[dev].load(std::memory_order_acquire)) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(KERN), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)bytes);
   if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev].store(1, std::memory_order_release);
   return e;
