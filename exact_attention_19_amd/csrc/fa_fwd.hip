@@ -291,23 +291,21 @@ __global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
 // Small-grid path for d = 64 (bf16): the key range is split over the four
 // waves of a workgroup, which all serve the same 32 query rows, so a short
 // batch still fills the chip (one wave per 32 rows left each wave walking
-// every key tile in series). Each step stages 128 keys as two 64-key tiles in
-// fwd_bf16_kernel's layout (K rows, V^T) and wave w takes their 32-key block
-// w, keeping its own running max (log2 units), sum and output. At the end the
-// four partial results merge through LDS with log-sum-exp weights:
-// O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w, m = max_w m_w.
+// every key tile in series). Each step covers 128 keys laid out as two 64-key
+// tiles in fwd_bf16_kernel's layout (K rows, V^T); wave w stages and reads
+// only their 32-key block w, so the waves never wait for each other inside
+// the loop, and keeps its own running max (log2 units), sum and output. At
+// the end the four partial results merge through LDS with log-sum-exp
+// weights: O = sum_w 2^(m_w - m) O_w / sum_w 2^(m_w - m) l_w, m = max_w m_w.
 template <bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
     int num_q_tiles) {
-  constexpr int D = 64, DS = 4, DB = 2, C8 = 8, NT = 256;
+  constexpr int D = 64, DS = 4, DB = 2, C8 = 8;
   using SM = FwdSmem<64, 4>;
   constexpr int TILE_ELEMS = SM::STAGE_ELEMS;          // one 64-key tile: K rows, then V^T
   constexpr int STEP_ELEMS = 2 * TILE_ELEMS;           // 128 keys per step
-  constexpr int K_CHUNKS = kBN * C8;                   // 512 16-byte chunks of one K tile
-  constexpr int K_PER_T = K_CHUNKS / NT;               // 2
-  constexpr int V_GROUPS = (kBN / 4) * C8;             // 128 (4 keys x 8 dims) groups of one V tile
   extern __shared__ __align__(16) unsigned char smem_raw[];
   __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
 
@@ -340,50 +338,43 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
   const int kv_end = CAUSAL ? min(N, q0 + 32) : N;
   const int n_steps = (kv_end + 127) / 128;
 
-  // Register staging of one step (two tiles); rows past N read row N - 1
-  // (their scores are masked, so the duplicates never count).
-  // Every thread issues the same number of loads (two K chunks of each tile,
-  // one V group of the step), so the compiler can wait for one step's loads
-  // while the next step's are in flight.
-  static_assert(2 * V_GROUPS == NT, "one V group of the step per thread");
-  const int v_ti = tid / V_GROUPS, v_g = tid % V_GROUPS;
-  u32x4 kA[2][K_PER_T], kB[2][K_PER_T];
+  // Each wave stages only its own 32-key block of every step (keys
+  // st*128 + 32*wave ..), in the step's shared tile layout, and reads only
+  // that block, so no barrier is needed between steps (a wave's LDS
+  // accesses complete in order). Register staging; rows past N read row
+  // N - 1 (their scores are masked, so the duplicates never count). Every
+  // lane issues the same loads, so the compiler can wait for one step's
+  // loads while the next step's are in flight.
+  const int ti_w = wave >> 1, kbk = wave & 1;  // this wave's tile and 32-key block within a step
+  constexpr int KW = 4;                         // K chunks per lane: 32 rows x 8 chunks / 64 lanes
+  const int v_kg = lane >> 3, v_dc = lane & 7;  // V group: keys 4*v_kg .. +3 of the block, dims 8*v_dc ..
+  u32x4 kA[KW], kB[KW];
   u32x4 vA[4], vB[4];
-  auto load_step = [&](int st, u32x4 (&kr)[2][K_PER_T], u32x4 (&vr)[4]) __attribute__((always_inline)) {
+  auto load_step = [&](int st, u32x4 (&kr)[KW], u32x4 (&vr)[4]) __attribute__((always_inline)) {
+    const int k0w = st * 128 + wave * 32;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      const int k0 = st * 128 + ti * kBN;
-#pragma unroll
-      for (int r = 0; r < K_PER_T; ++r) {
-        const int c = tid + r * NT;
-        const int row = c / C8, col = c % C8;
-        kr[ti][r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)min(k0 + row, N - 1) * kv_rs + col * 8);
-      }
+    for (int r = 0; r < KW; ++r) {
+      const int c = lane + 64 * r;
+      kr[r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)min(k0w + c / C8, N - 1) * kv_rs + (c % C8) * 8);
     }
-    const int k0 = st * 128 + v_ti * kBN + (v_g / C8) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)min(k0 + i, N - 1) * kv_rs + (v_g % C8) * 8);
+      vr[i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)min(k0w + 4 * v_kg + i, N - 1) * kv_rs + v_dc * 8);
   };
-  auto store_step = [&](int stage, const u32x4 (&kr)[2][K_PER_T], const u32x4 (&vr)[4])
-                        __attribute__((always_inline)) {
+  auto store_step = [&](int stage, const u32x4 (&kr)[KW], const u32x4 (&vr)[4]) __attribute__((always_inline)) {
+    __bf16* ks = smem + stage * STEP_ELEMS + ti_w * TILE_ELEMS;
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
-      __bf16* ks = smem + stage * STEP_ELEMS + ti * TILE_ELEMS;
-#pragma unroll
-      for (int r = 0; r < K_PER_T; ++r) {
-        const int c = tid + r * NT;
-        *reinterpret_cast<u32x4*>(ks + (c / C8) * SM::KS + (c % C8) * 8) = kr[ti][r];
-      }
+    for (int r = 0; r < KW; ++r) {
+      const int c = lane + 64 * r;
+      *reinterpret_cast<u32x4*>(ks + (kbk * 32 + c / C8) * SM::KS + (c % C8) * 8) = kr[r];
     }
-    store_transposed_4x8(smem + stage * STEP_ELEMS + v_ti * TILE_ELEMS + SM::K_ELEMS, v_g / C8, v_g % C8, vr);
+    store_transposed_4x8(ks + SM::K_ELEMS, 8 * kbk + v_kg, v_dc, vr);
   };
 
   f32x16 oacc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
-  const int ti_w = wave >> 1, kbk = wave & 1;  // this wave's tile and 32-key block within a step
 
   auto compute = [&](int st) __attribute__((always_inline)) {
     const int k0b = st * 128 + wave * 32;
@@ -442,23 +433,22 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
   load_step(0, kA, vA);
   load_step(1, kB, vB);
   store_step(0, kA, vA);
-  __syncthreads();
   for (int st = 0; st < n_steps; st += 2) {
     load_step(st + 2, kA, vA);
     compute(st);
     if (st + 1 < n_steps) store_step(1, kB, vB);
-    __syncthreads();
     if (st + 1 >= n_steps) break;
     load_step(st + 3, kB, vB);
     compute(st + 1);
     if (st + 2 < n_steps) store_step(0, kA, vA);
-    __syncthreads();
   }
+  __syncthreads();  // every wave is done with the staging area before the merge reuses it
 
   // Merge through LDS (the stages are free after the last barrier): partial
   // O [4][32][64] fp32, then max and sum [4][32].
+  constexpr int PO = D + 4;  // padded row stride of the partial outputs (no bank conflicts)
   float* part_o = reinterpret_cast<float*>(smem_raw);
-  float* part_m = part_o + 4 * 32 * D;
+  float* part_m = part_o + 4 * 32 * PO;
   float* part_l = part_m + 4 * 32;
   const float l_tot = pair_sum(l_run);
 #pragma unroll
@@ -468,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
       f32x4 w4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) w4[i] = oacc[db][4 * j + i];
-      *reinterpret_cast<f32x4*>(part_o + (wave * 32 + l32) * D + db * 32 + 8 * j + 4 * hh) = w4;
+      *reinterpret_cast<f32x4*>(part_o + (wave * 32 + l32) * PO + db * 32 + 8 * j + 4 * hh) = w4;
     }
   }
   if (hh == 0) {
@@ -488,8 +478,8 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
     const float mw = part_m[w * 32 + qi];
     const float c = (mw == kNegInf) ? 0.f : fast_exp2(mw - m);
     wsum += c * part_l[w * 32 + qi];
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(part_o + (w * 32 + qi) * D + dc);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(part_o + (w * 32 + qi) * D + dc + 4);
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(part_o + (w * 32 + qi) * PO + dc);
+    const f32x4 x1 = *reinterpret_cast<const f32x4*>(part_o + (w * 32 + qi) * PO + dc + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[i] += c * x0[i];
