@@ -317,6 +317,23 @@ def extras(fa_mod, lib, dev):
         del o_, l_
         del q, k, v
     out["fwd_sweep_h2048"] = {"workload": "causal forward, H=16 d=128, B*N = 16384 tokens", "points": sweep}
+    # The same sweep at head dim 64 (hidden 2048 = 32 heads x 64), causal and not.
+    sweep = {}
+    for N in (512, 2048, 8192, 16384):
+        for causal in (True, False):
+            B = 16384 // N
+            inp = workloads.prefill_inputs(B, N, 32, 32, 64, "bf16", seed=6, mult=0.5)
+            q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+            del inp
+            o_, l_ = torch.empty_like(q), torch.empty((B, 32, N), dtype=torch.float32, device=dev)
+            t = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=causal, out=o_, lse=l_))
+            pairs = _pairs_band(N, N, causal) * B * 32
+            tf = 4 * 64 * pairs / (t["ms"] * 1e9)
+            sweep[f"N={N} B={B}{' causal' if causal else ''}"] = {**t, "TFLOP/s": round(tf, 1),
+                                                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del o_, l_
+            del q, k, v
+    out["fwd_sweep_h2048_d64"] = {"workload": "forward, H=32 d=64, B*N = 16384 tokens", "points": sweep}
     # The two small configs: an fp32 forward (B=1, H=1, N=128, d=64, non-causal)
     # and a bf16 d=64 forward (B=2, H=8, N=1024, non-causal and causal). Both
     # are a few workgroups and launch-bound; they are timed through the C ABI

@@ -183,6 +183,20 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 
 __device__ __forceinline__ int tile_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// The same tiles for d = 64: 128-byte rows of eight 16-byte units. With
+// m = r / 2, unit u of row r lands at u ^ (4 (m & 1) + (m / 2) % 4). Over
+// eight consecutive rows of one parity this is a permutation of 0..7, so
+// 16-byte operand reads down 16 consecutive rows meet 16 distinct bank
+// groups (odd rows sit in the other half of the 256-byte bank line); over
+// rows c, c + 2, c + 4, c + 6 its bit 2 alternates, so a transposed read of
+// a 4-row block uses both halves of the row evenly.
+__device__ __forceinline__ int tile_swz8(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+template <int D>
+__device__ __forceinline__ int row_swz(int r) {
+  static_assert(D == 64 || D == 128, "d = 64 or 128");
+  return D == 128 ? tile_swz(r) : tile_swz8(r);
+}
+
 // Scalar (wave-uniform) copy of a value the compiler cannot prove uniform,
 // e.g. the result of an integer division of uniform operands.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -208,6 +222,16 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int lane, int first, uint32_
   return (uint32_t)lr * stride_bytes + 16u * (uint32_t)((lane & 15) ^ tile_swz(4 * first + lr));
 }
 
+// The same for tiles of D-dim rows: a 1 KB chunk holds 1024 / (2 D) rows
+// (4 at d = 128, 8 at d = 64); for d = 64 the chunks a wave issues,
+// c = first + 4 i, share the swizzle phase of rows 8 c + (0..7).
+template <int D>
+__device__ __forceinline__ uint32_t dma_lane_offset_d(int lane, int first, uint32_t stride_bytes) {
+  if constexpr (D == 128) return dma_lane_offset(lane, first, stride_bytes);
+  const int lr = lane >> 3;
+  return (uint32_t)lr * stride_bytes + 16u * (uint32_t)((lane & 7) ^ tile_swz8(8 * first + lr));
+}
+
 // Tile DMA: rows [0, 64) below `tile_base` (row stride `stride_bytes`) go
 // into a swizzled LDS tile; rows at or past `nrows` arrive as zeros. The
 // calling wave issues chunks c = first + step*i (4 rows each, i < nchunk,
@@ -225,6 +249,24 @@ __device__ __forceinline__ void dma_rows64(const unsigned char* tile_base, uint3
   const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform(tile_base), rows * stride_bytes);
   const uint32_t chunk_stride = (uint32_t)(4 * step) * stride_bytes;
   const uint32_t first_off = lane_off + (uint32_t)(4 * first) * stride_bytes;
+#pragma unroll
+  for (int i = 0; i < nchunk; ++i) {
+    const int c = first + step * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds_tile + c * 1024), 16, first_off + i * chunk_stride,
+                                             0, 0, 0);
+  }
+}
+
+// dma_rows64 for tiles of D-dim rows (1024 / (2 D) rows per chunk).
+template <int D>
+__device__ __forceinline__ void dma_rows64_d(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
+                                             unsigned char* lds_tile, int first, int step, int nchunk,
+                                             uint32_t lane_off) {
+  constexpr int RPC = 1024 / (2 * D);
+  const uint32_t rows = (uint32_t)uniform(min(max(nrows, 0), 64));
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(uniform(tile_base), rows * stride_bytes);
+  const uint32_t chunk_stride = (uint32_t)(RPC * step) * stride_bytes;
+  const uint32_t first_off = lane_off + (uint32_t)(RPC * first) * stride_bytes;
 #pragma unroll
   for (int i = 0; i < nchunk; ++i) {
     const int c = first + step * i;

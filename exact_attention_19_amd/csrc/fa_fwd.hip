@@ -41,6 +41,10 @@ constexpr float kSumLimit = 256.f;
 #define SGB_VALU 6
 #endif
 
+// Register-staged 64-key tile of the d = 64 split-key kernel: K rows (padded
+// row stride), then V^T (D rows of kBN keys, stored transposed by
+// store_transposed_4x8 in the order the score accumulator hands keys to the
+// P V product).
 template <int D, int NWAVES>
 struct FwdSmem {
   static constexpr int KS = D + 8;                      // K row stride (elements), 16-byte pad
@@ -50,249 +54,11 @@ struct FwdSmem {
   static constexpr int BYTES = 2 * STAGE_ELEMS * 2;     // two stages, bf16
 };
 
-template <int D, int NWAVES, bool CAUSAL>
-__global__ __launch_bounds__(NWAVES * 64, 2) void fwd_bf16_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N,
-    float scale_log2, int num_q_tiles) {
-  constexpr int BM = NWAVES * 32;
-  constexpr int NT = NWAVES * 64;
-  constexpr int DS = D / 16;      // MFMA k-steps over the head dim
-  constexpr int DB = D / 32;      // 32-row blocks of O^T
-  constexpr int C8 = D / 8;       // 16-byte chunks per row
-  using SM = FwdSmem<D, NWAVES>;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  // Heaviest causal tiles first; consecutive workgroups take different heads.
-  const int BH = B * Hq;
-  const int bid = blockIdx.x;
-  const int bh = bid % BH;
-  const int rank = bid / BH;
-  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
-
-  const int64_t q_row_stride = (int64_t)Hq * D;
-  const int64_t kv_row_stride = (int64_t)Hkv * D;
-  const __bf16* qb = q + ((int64_t)b * N) * q_row_stride + (int64_t)hq * D;
-  const __bf16* kb = k + ((int64_t)b * N) * kv_row_stride + (int64_t)hk * D;
-  const __bf16* vb = v + ((int64_t)b * N) * kv_row_stride + (int64_t)hk * D;
-
-  const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;          // first query row of this wave
-  const int my_q = qw0 + l32;              // query row of this lane
-  const bool wave_active = qw0 < N;
-
-  // Q fragments: B operand of S^T = K Q^T. Lane holds Q[my_q][16 s + 8 hh .. +7].
-  // Rows past N read row N-1 instead (their results are never written), so
-  // no load is predicated.
-  bf16x8 qf[DS];
-  {
-    const __bf16* qrow = qb + (int64_t)min(my_q, N - 1) * q_row_stride + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * s));
-    }
-  }
-
-  int kv_end = N;
-  if (CAUSAL) kv_end = min(N, q0 + BM);
-  const int n_tiles = (kv_end + kBN - 1) / kBN;
-
-  // Global -> register staging of one K/V tile.
-  constexpr int K_CHUNKS = kBN * C8;                 // 16-byte chunks of the K tile
-  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-  constexpr int V_GROUPS = (kBN / 4) * C8;           // (4 keys x 8 dims) groups of V
-  constexpr int V_PER_T = (V_GROUPS + NT - 1) / NT;
-  // Two register sets, so that a tile's loads are in flight for a whole
-  // step (tile t + 2 is requested while tile t is computed and tile t + 1,
-  // requested one step earlier, is stored to LDS).
-  u32x4 kregA[K_PER_T], kregB[K_PER_T];
-  u32x4 vregA[V_PER_T][4], vregB[V_PER_T][4];
-
-  // Key rows past N are read as row N-1: their scores are masked to -inf and
-  // their probabilities are exactly 0, so the duplicate values never count.
-  auto load_tile = [&](int t, u32x4 (&kreg)[K_PER_T], u32x4 (&vreg)[V_PER_T][4]) {
-    const int k0 = t * kBN;
-#pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int c = tid + r * NT;
-      const int row = c / C8, col = c % C8;
-      const int key = min(k0 + row, N - 1);
-      if (K_CHUNKS % NT == 0 || c < K_CHUNKS)
-        kreg[r] = *reinterpret_cast<const u32x4*>(kb + (int64_t)key * kv_row_stride + col * 8);
-    }
-#pragma unroll
-    for (int r = 0; r < V_PER_T; ++r) {
-      const int g = tid + r * NT;
-      const int dc = g % C8, kg = g / C8;
-      if (V_GROUPS % NT == 0 || g < V_GROUPS) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(k0 + kg * 4 + i, N - 1);
-          vreg[r][i] = *reinterpret_cast<const u32x4*>(vb + (int64_t)key * kv_row_stride + dc * 8);
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&](int stage, const u32x4 (&kreg)[K_PER_T], const u32x4 (&vreg)[V_PER_T][4]) {
-    __bf16* ks = smem + stage * SM::STAGE_ELEMS;
-    __bf16* vt = ks + SM::K_ELEMS;
-#pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int c = tid + r * NT;
-      if (c < K_CHUNKS) {
-        const int row = c / C8, col = c % C8;
-        *reinterpret_cast<u32x4*>(ks + row * SM::KS + col * 8) = kreg[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < V_PER_T; ++r) {
-      const int g = tid + r * NT;
-      if (g < V_GROUPS) {
-        store_transposed_4x8(vt, g / C8, g % C8, vreg[r]);
-      }
-    }
-  };
-
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) oacc[i] = f32x16{};
-  float m_run = kNegInf;  // running max of the scaled scores (log2 units)
-  float l_run = 0.f;      // this lane's share of the running exp-sum
-
-  auto compute = [&](int t) __attribute__((always_inline)) {
-    const int stage = t & 1;
-    const int k0 = t * kBN;
-    const bool wave_skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
-    if (!wave_skip) {
-      const __bf16* ks = smem + stage * SM::STAGE_ELEMS;
-      const __bf16* vt = ks + SM::K_ELEMS;
-      // S^T for the two 32-key blocks of the tile.
-      f32x16 sacc[2];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-        sacc[kbk] = f32x16{};
-        const __bf16* krow = ks + (kbk * 32 + l32) * SM::KS + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * s);
-          sacc[kbk] = mfma32(a, qf[s], sacc[kbk]);
-        }
-      }
-      // Row maximum of the raw (unscaled) scores; masked entries are -inf.
-      const bool need_mask = (CAUSAL && (k0 + kBN - 1 > qw0)) || (k0 + kBN > N);
-      float mt = kNegInf;
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float x = sacc[kbk][e];
-          if (need_mask) {
-            const int key = k0 + kbk * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const bool masked = (key >= N) || (CAUSAL && key > my_q);
-            x = masked ? kNegInf : x;
-            sacc[kbk][e] = x;
-          }
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = pair_max(mt) * scale_log2;  // log2 units (scale > 0)
-      // Lazy rescale: the reference maximum m_run only moves when some row's
-      // maximum exceeds it by more than kRescaleSlack, so p <= 2^kRescaleSlack.
-      // O and l always share the same reference, so the result is unchanged;
-      // most tiles skip the O *= alpha pass entirely.
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-        }
-      }
-      const float neg_m = (m_run == kNegInf) ? 0.f : -m_run;
-      float psum = 0.f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = fast_exp2(fmaf(sacc[kbk][e], scale_log2, neg_m));
-          psum += p;
-          pb[kbk * 2 + (e >> 3)][e & 7] = (__bf16)p;
-        }
-      }
-      l_run += psum;
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int d = db * 32 + l32;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          bf16x8 a = load_tr_operand(vt, d, st, hh);
-          oacc[db] = mfma32(a, pb[st], oacc[db]);
-        }
-      }
-    }
-  };
-
-  load_tile(0, kregA, vregA);
-  if (n_tiles > 1) load_tile(1, kregB, vregB);
-  store_tile(0, kregA, vregA);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
-    // Tile t is in stage 0, tile t + 1 in register set B.
-    if (t + 2 < n_tiles) load_tile(t + 2, kregA, vregA);
-    compute(t);
-    if (t + 1 < n_tiles) store_tile(1, kregB, vregB);
-    __syncthreads();
-    if (t + 1 >= n_tiles) break;
-    // Tile t + 1 is in stage 1, tile t + 2 in register set A.
-    if (t + 3 < n_tiles) load_tile(t + 3, kregB, vregB);
-    compute(t + 1);
-    if (t + 2 < n_tiles) store_tile(0, kregA, vregA);
-    __syncthreads();
-  }
-
-  if (!wave_active) return;
-  const float l_tot = pair_sum(l_run);
-  if (my_q < N) {
-    const bool empty = !(l_tot > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_tot;
-    __bf16* orow = o + ((int64_t)b * N + my_q) * q_row_stride + (int64_t)hq * D;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * j + 4 * hh) = w;
-      }
-    }
-    if (hh == 0) {
-      lse[((int64_t)b * Hq + hq) * N + my_q] = empty ? kNegInf : (m_run + __log2f(l_tot)) * kLn2;
-    }
-  }
-}
-
 // Small-grid path for d = 64 (bf16): the key range is split over the four
 // waves of a workgroup, which all serve the same 32 query rows, so a short
 // batch still fills the chip (one wave per 32 rows left each wave walking
 // every key tile in series). Each step covers 128 keys laid out as two 64-key
-// tiles in fwd_bf16_kernel's layout (K rows, V^T); wave w stages and reads
+// FwdSmem tiles (K rows, V^T); wave w stages and reads
 // only their 32-key block w, so the waves never wait for each other inside
 // the loop, and keeps its own running max (log2 units), sum and output. At
 // the end the four partial results merge through LDS with log-sum-exp
@@ -498,8 +264,9 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
   }
 }
 
-// bf16 path for d = 128. K and V tiles go from global memory straight into
-// swizzled row-major LDS tiles (no staging registers, no transposing stores);
+// bf16 path for d = 128 and (dense batches) d = 64. K and V tiles go from
+// global memory straight into swizzled row-major LDS tiles (no staging
+// registers, no transposing stores; rows of 2 d bytes, swizzled by row_swz);
 // the V^T operand of the P V product is read with ds_read_b64_tr_b16, whose
 // 4-row blocks are exactly the key groups the score accumulator hands to one
 // 16-key MFMA step: elements 0-3 are keys 16*st + 4*hh + {0..3}, elements
@@ -509,22 +276,23 @@ __global__ __launch_bounds__(256, 2) void fwd_splitk_d64_kernel(
 // read from LDS feeds QB MFMAs (one per query block), so LDS read traffic per
 // MFMA falls as 1/QB; with QB = 2 the O accumulators (128 registers) and the
 // Q operands (64) need one wave per SIMD.
-template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d128_kernel(
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE, int D = 128>
+__global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? (D == 64 ? 3 * 4 : 8) : 4) / NWAVES) void fwd_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int B, int Hq, int Hkv, int N, float scale_log2,
     int num_q_tiles, FwdSeq seq) {
   constexpr bool VARLEN = (MODE & kModeVarlen) != 0;
   constexpr bool WINDOW = (MODE & kModeWindow) != 0;
   constexpr bool BSPARSE = (MODE & kModeBlockSparse) != 0;
-  constexpr int D = 128;
+  static_assert(D == 128 || (D == 64 && MODE == 0 && QB == 1), "d = 64: dense batches, one query block per wave");
+  constexpr int ROWB = 2 * D;           // bytes of one tile row
   constexpr int WQ = 32 * QB;           // query rows per wave
   constexpr int BM = NWAVES * WQ;       // query rows per workgroup
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int TILE = 64 * 256;        // bytes of one 64 x 128 bf16 tile
+  constexpr int TILE = 64 * ROWB;       // bytes of one 64 x D bf16 tile
   constexpr int STAGE = 2 * TILE;       // K tile then V tile
-  constexpr int CPW = 16 / NWAVES;      // 1 KB chunks per wave per tile
+  constexpr int CPW = TILE / 1024 / NWAVES;  // 1 KB chunks per wave per tile
   static_assert(!BSPARSE || (BM == kBlockSparseBlock && !VARLEN && !WINDOW),
                 "block-sparse mode: one 128-row query block per workgroup, dense batch");
   extern __shared__ __align__(1024) unsigned char smem[];
@@ -603,7 +371,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   // Per-lane LDS byte offsets inside a tile (constant over the loop).
   // K operand (A of S^T): row 32*kbk + l32, logical unit 2*s + hh.
   //   offset = row*256 + 16*((2s + hh) ^ swz(row)) = koff ^ (32*s) + kbk*8192.
-  const int koff = l32 * 256 + 16 * (hh ^ tile_swz(l32));
+  const int koff = l32 * ROWB + 16 * (hh ^ row_swz<D>(l32));
   // V^T operand (A of O^T): tr reads at rows 16*st + 4*hh + j/4 (+8), column
   // block 32*db + 16*(g&1) + 4*(j&3), j = lane & 15, g = lane >> 4.
   int voff[2];
@@ -613,7 +381,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     for (int rd = 0; rd < 2; ++rd) {
       const int r = 4 * hh + (j >> 2) + 8 * rd;
       const int unit = 2 * (g & 1) + ((j & 3) >> 1);  // db = 0
-      voff[rd] = r * 256 + 16 * (unit ^ tile_swz(r)) + 8 * (j & 1);
+      voff[rd] = r * ROWB + 16 * (unit ^ row_swz<D>(r)) + 8 * (j & 1);
     }
   }
 
@@ -628,14 +396,15 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
   }
 
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
-  const uint32_t dma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
+  const uint32_t dma_off = dma_lane_offset_d<D>(lane, wave, kv_rs_bytes);
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * 64 * kv_rs * 2;
     const int nrows = Nk - t * 64;
-    dma_rows64(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, CPW, dma_off);
-    dma_rows64(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES, CPW,
-               dma_off);
+    dma_rows64_d<D>(reinterpret_cast<const unsigned char*>(kb) + off, kv_rs_bytes, nrows, st, wave, NWAVES, CPW,
+                    dma_off);
+    dma_rows64_d<D>(reinterpret_cast<const unsigned char*>(vb) + off, kv_rs_bytes, nrows, st + TILE, wave, NWAVES,
+                    CPW, dma_off);
   };
 
   // A 64-key tile is two 32-key blocks, skewed so that independent work sits
@@ -649,7 +418,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     for (int j = 0; j < QB; ++j) r.s[j] = f32x16{};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (koff ^ (32 * s)));
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + kbk * 32 * ROWB + (koff ^ (32 * s)));
 #pragma unroll
       for (int j = 0; j < QB; ++j) r.s[j] = mfma32(a, qf[j][s], r.s[j]);
     }
@@ -712,8 +481,8 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int st = 2 * kbk + tt;
-        const i16x4 lo = tr_read(vs + st * 4096 + (voff[0] ^ (64 * db)));
-        const i16x4 hi = tr_read(vs + st * 4096 + (voff[1] ^ (64 * db)));
+        const i16x4 lo = tr_read(vs + st * 16 * ROWB + (voff[0] ^ (64 * db)));
+        const i16x4 hi = tr_read(vs + st * 16 * ROWB + (voff[1] ^ (64 * db)));
         const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int j = 0; j < QB; ++j) oacc[j][db] = mfma32(a, pr[j].pb[tt], oacc[j][db]);
@@ -962,7 +731,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
     const float l_tot = pair_sum(l_run[0]);
     const bool empty = !(l_tot > 0.f);
     const float inv = empty ? 0.f : 1.f / l_tot;
-    unsigned char* ot = smem + wave * 8192;
+    unsigned char* ot = smem + wave * 32 * ROWB;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -970,14 +739,16 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? 8 : 4) / NWAVES) void fwd_d
         u32x2 w;
         w[0] = pack_bf16x2(oacc[0][db][4 * i + 0] * inv, oacc[0][db][4 * i + 1] * inv);
         w[1] = pack_bf16x2(oacc[0][db][4 * i + 2] * inv, oacc[0][db][4 * i + 3] * inv);
-        *reinterpret_cast<u32x2*>(ot + l32 * 256 + 16 * ((4 * db + i) ^ tile_swz(l32)) + 8 * hh) = w;
+        *reinterpret_cast<u32x2*>(ot + l32 * ROWB + 16 * ((4 * db + i) ^ row_swz<D>(l32)) + 8 * hh) = w;
       }
     }
-    const int unit = lane & 15;
+    constexpr int UNITS = D / 8;              // 16-byte units per row
+    constexpr int RPI = 64 / UNITS;           // rows per wave instruction
+    const int unit = lane % UNITS;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int row = 4 * c + (lane >> 4);
-      const u32x4 val = *reinterpret_cast<const u32x4*>(ot + row * 256 + 16 * (unit ^ tile_swz(row)));
+    for (int c = 0; c < 32 / RPI; ++c) {
+      const int row = RPI * c + lane / UNITS;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ot + row * ROWB + 16 * (unit ^ row_swz<D>(row)));
       if (qw0 + row < Nq)
         *reinterpret_cast<u32x4*>(o + ((int64_t)q_start + qw0 + row) * q_rs + (int64_t)hq * D + 8 * unit) = val;
     }
@@ -1087,23 +858,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(
   }
 }
 
-template <int D, int NWAVES, bool CAUSAL>
-hipError_t launch_bf16(const FwdArgs& a) {
-  constexpr int BM = NWAVES * 32;
-  const int num_q_tiles = (a.N + BM - 1) / BM;
-  const int64_t grid = (int64_t)num_q_tiles * a.B * a.Hq;
-  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const size_t smem = FwdSmem<D, NWAVES>::BYTES;
-  auto kern = fwd_bf16_kernel<D, NWAVES, CAUSAL>;
-  hipError_t e = set_smem_once<fwd_bf16_kernel<D, NWAVES, CAUSAL>>(smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
-                     a.B, a.Hq, a.Hkv, a.N, a.scale * kLog2e, num_q_tiles);
-  return hipGetLastError();
-}
-
-template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE = 0>
+template <int NWAVES, int NSTAGE, int QB, bool CAUSAL, int MODE = 0, int D = 128>
 hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   constexpr int BM = NWAVES * 32 * QB;
   const int rows = (MODE & kModeVarlen) ? seq.max_q : a.N;
@@ -1112,10 +867,10 @@ hipError_t launch_d128(const FwdArgs& a, const FwdSeq& seq = FwdSeq{}) {
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Tile ring, then (QB > 1) one 4 KB rescale slot per wave or (block-sparse)
   // the active-tile list and its count.
-  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 256 + (QB > 1 ? NWAVES * 4096 : 0) +
+  constexpr size_t smem = (size_t)NSTAGE * 2 * 64 * 2 * D + (QB > 1 ? NWAVES * 4096 : 0) +
                           ((MODE & kModeBlockSparse) ? 2 * 2 * kBlockSparseMaxBlocks + 16 : 0);
-  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>;
-  hipError_t e = set_smem_once<fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE>>(smem);
+  auto kern = fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE, D>;
+  hipError_t e = set_smem_once<fwd_d128_kernel<NWAVES, NSTAGE, QB, CAUSAL, MODE, D>>(smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NWAVES * 64), smem, a.stream,
                      (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.o, a.lse,
@@ -1159,9 +914,11 @@ hipError_t launch_fwd(const FwdArgs& a) {
     // key range over the waves of 32-row workgroups instead (measured 1.2-1.7x
     // faster at B=2, H=8, N=1024; 2x slower than the 128-row kernel once the
     // grid is large, where the split quadruples the K/V reads per query).
+    // Otherwise the DMA kernel of d = 128 with 128-byte rows (161 registers,
+    // so three workgroups share a CU).
     if ((int64_t)a.B * a.Hq * ((a.N + 127) / 128) <= kSplitKMaxWorkgroups)
       return a.causal ? launch_splitk64<true>(a) : launch_splitk64<false>(a);
-    return a.causal ? launch_bf16<64, 4, true>(a) : launch_bf16<64, 4, false>(a);
+    return a.causal ? launch_d128<4, 2, 1, true, 0, 64>(a) : launch_d128<4, 2, 1, false, 0, 64>(a);
   }
   return a.causal ? launch_d128<4, 2, 1, true>(a) : launch_d128<4, 2, 1, false>(a);
 }

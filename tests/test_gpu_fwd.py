@@ -59,7 +59,9 @@ SWEEP = [
     (1, 333, 16, 2, 64),
     (1, 2113, 2, 1, 128),
     (1, 2113, 2, 1, 64),     # d = 64, key range split over the waves, 17 steps of 128 keys
-    (4, 1100, 16, 4, 64),    # d = 64 with 576 workgroups of 128 rows: the unsplit kernel
+    (4, 1100, 16, 4, 64),    # d = 64 with 576 workgroups of 128 rows: the DMA kernel with 128-byte rows
+    (2, 1500, 16, 2, 64),    # d = 64 DMA kernel: ragged last tile, 8 query heads per kv head
+    (3, 900, 12, 3, 64),     # d = 64 DMA kernel: 288 workgroups, B = 3, 4 query heads per kv head
 ]
 
 

@@ -71,6 +71,28 @@ def test_causal_sweep_hidden2048(N):
     _check_fwd_sampled(inp, o.cpu(), lse.cpu(), w, heads, rng)
 
 
+@pytest.mark.parametrize("N,causal", [(2048, True), (2048, False), (16384, True)])
+def test_sweep_d64_hidden2048(N, causal):
+    """Head dim 64 (32 heads x 64 = hidden 2048, 16k tokens per batch), inputs
+    N(0,1)*0.5, through the DMA kernel with 128-byte rows: every output
+    written, sampled rows of every head of two batches against the oracle."""
+    fa = need_gpu()
+    w = workloads.sweep_d64(N, causal)
+    announce(f"large fwd d64 sweep N={N} B={w.B} causal={causal}")
+    dev = torch.device("cuda:0")
+    inp = workloads.prefill_inputs(w.B, w.N, w.Hq, w.Hkv, w.d, "bf16", seed=1, mult=w.mult)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = _nan_outputs(q, w.B, w.Hq, w.N)
+    fa.fa_fwd(q, k, v, scale=w.scale, causal=causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    if causal:
+        assert torch.equal(o[:, 0], v[:, 0])
+    rng = np.random.default_rng(N + int(causal))
+    heads = [(b, h) for b in sorted({0, w.B - 1}) for h in range(w.Hq)]
+    _check_fwd_sampled(inp, o.cpu(), lse.cpu(), w, heads, rng)
+
+
 def _c4_inputs(hkv):
     w = workloads.WORKLOADS["c4" if hkv == 96 else "c4g"]
     inp = workloads.prefill_inputs(w.B, w.N, w.Hq, w.Hkv, w.d, "bf16", seed=0, with_do=True)

@@ -124,6 +124,13 @@ def c3(N: int) -> Workload:
                     note="hidden 2048 = 16 heads x 128, 16k tokens per batch")
 
 
+def sweep_d64(N: int, causal: bool = True) -> Workload:
+    """The head-dim-64 member of the same benchmark sweep: hidden 2048 = 32
+    heads x 64, 16k tokens per batch."""
+    return Workload(f"sweep_d64_{'causal_' if causal else ''}fwd_N{N}", "fwd", 16384 // N, 32, 32, N, 64, "bf16",
+                    causal, 0.5, note="hidden 2048 = 32 heads x 64, 16k tokens per batch")
+
+
 WORKLOADS = {
     "c1": Workload("c1_fp32_fwd", "fwd", 1, 1, 1, 128, 64, "fp32", False),
     "c2": Workload("c2_bf16_fwd", "fwd", 2, 8, 8, 1024, 64, "bf16", False),
