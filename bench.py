@@ -65,6 +65,9 @@ def parse():
                          "adds steps outside the timed region)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the secondary measurements (window, varlen, paged decode, block-sparse)")
+    ap.add_argument("--sweep-only", type=int, default=0, metavar="LAUNCHES",
+                    help="only run the causal forward sweep (H=16, d=128, 16k tokens at N = 512, 2048, 8192, "
+                         "16384), LAUNCHES launches per point after two warm-up launches, and exit (profiling)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -84,6 +87,33 @@ def copy_calibration(mib: int) -> None:
         torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": 4 * n, "launches": 3}))
+
+
+def sweep_only(launches: int) -> None:
+    """The causal forward sweep of the extras (same inputs), `launches`
+    back-to-back launches per point after two warm-up launches, for a
+    profiler to take apart point by point (the launches run in the order
+    N = 512, 2048, 8192, 16384)."""
+    import torch
+
+    import exact_attention_19_amd as fa
+    import workloads
+
+    fa.load()
+    dev = torch.device("cuda:0")
+    done = {}
+    for N in (512, 2048, 8192, 16384):
+        B = 16384 // N
+        inp = workloads.prefill_inputs(B, N, 16, 16, 128, "bf16", seed=5, mult=0.5)
+        q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+        del inp
+        o_, l_ = torch.empty_like(q), torch.empty((B, 16, N), dtype=torch.float32, device=dev)
+        for _ in range(2 + launches):
+            fa.fa_fwd(q, k, v, causal=True, out=o_, lse=l_)
+        torch.cuda.synchronize()
+        done[f"N={N} B={B}"] = 2 + launches
+        del q, k, v, o_, l_
+    print(json.dumps({"sweep_only_launches": done}))
 
 
 def source_sha(name: str) -> str:
@@ -455,6 +485,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.sweep_only:
+        sweep_only(args.sweep_only)
         return
 
     import numpy as np
