@@ -327,3 +327,26 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     vv = np.asarray(v[b, :, kh, :], dtype=np.float64)
     _, p, lse = head_probs(qh, kk, scale, causal, rows=rows, nq=q.shape[1])
     return p @ vv, lse
+
+
+def attn_bwd_dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
+    """dQ and D for selected query rows of one (batch, query head).
+
+    Row i of dQ depends only on row i of P and of dP (the backward formulas
+    in the module docstring: D_i = sum_j P_ij dP_ij, dS_i = P_i (dP_i - D_i),
+    dQ_i = scale dS_i K), so sampled rows cost O(len(rows) * Nk * d) and
+    check problems too large for the full backward. Returns
+    (dq [len(rows), d], D [len(rows)]).
+    """
+    hq, hkv = q.shape[2], k.shape[2]
+    kv_head = h // _check_heads(hq, hkv)
+    rows = np.asarray(rows)
+    qr = np.asarray(q[b, rows, h, :], dtype=np.float64)
+    dor = np.asarray(do[b, rows, h, :], dtype=np.float64)
+    kk = np.asarray(k[b, :, kv_head, :], dtype=np.float64)
+    vv = np.asarray(v[b, :, kv_head, :], dtype=np.float64)
+    _, pr, _ = head_probs(qr, kk, scale, causal, rows=rows, nq=q.shape[1])
+    dpr = dor @ vv.T
+    dr = (pr * dpr).sum(axis=1)
+    dsr = pr * (dpr - dr[:, None])
+    return scale * (dsr @ kk), dr

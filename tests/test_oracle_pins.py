@@ -594,6 +594,50 @@ def pin_window_finite_differences(m):
                     assert err < 1e-6, (name, window, causal, err)
 
 
+def pin_bwd_dq_rows(m):
+    """Sampled-row dQ and D (used for checks too large for the full backward)
+    agree with the full backward, with GQA, causal and not, and Nq != Nk
+    (bottom-right causal alignment)."""
+    rng = np.random.default_rng(31)
+    for (B, nq, nk, hq, hkv) in [(2, 9, 9, 4, 2), (1, 6, 10, 2, 1)]:
+        q, k, v = _rand(rng, B, nq, hq, 3), _rand(rng, B, nk, hkv, 3), _rand(rng, B, nk, hkv, 3)
+        do = _rand(rng, B, nq, hq, 3)
+        for causal in (False, True):
+            dq, _, _, dd = m.attn_bwd(q, k, v, do, 0.8, causal)
+            rows = [0, nq // 2, nq - 1]
+            for b in range(B):
+                for h in range(hq):
+                    rq, rd = m.attn_bwd_dq_rows(q, k, v, do, 0.8, causal, b, h, rows)
+                    np.testing.assert_allclose(rq, dq[b, rows, h], rtol=0, atol=1e-13)
+                    np.testing.assert_allclose(rd, dd[b, h, rows], rtol=0, atol=1e-13)
+
+
+def pin_bwd_dq_rows_finite_differences(m):
+    """Central differences of sum(O * dO) with respect to the sampled query
+    rows, through the forward (itself pinned by brute force), against the
+    sampled-row dQ, with GQA, causal and not."""
+    rng = np.random.default_rng(32)
+    hstep = 1e-6
+    B, nq, nk, hq, hkv, d = 1, 5, 7, 2, 1, 3
+    q, k, v = _rand(rng, B, nq, hq, d), _rand(rng, B, nk, hkv, d), _rand(rng, B, nk, hkv, d)
+    do = _rand(rng, B, nq, hq, d)
+    rows = [0, 2, 4]
+    for causal in (False, True):
+        def loss(qq):
+            return float((m.attn_fwd(qq, k, v, 0.7, causal)[0] * do).sum())
+        for h in range(hq):
+            rq, _ = m.attn_bwd_dq_rows(q, k, v, do, 0.7, causal, 0, h, rows)
+            for ri, i in enumerate(rows):
+                for c in range(d):
+                    qp, qm = q.copy(), q.copy()
+                    qp[0, i, h, c] += hstep
+                    qm[0, i, h, c] -= hstep
+                    num = (loss(qp) - loss(qm)) / (2 * hstep)
+                    assert abs(num - rq[ri, c]) < 1e-6 * max(1.0, abs(rq[ri, c])), (causal, h, i, c, num, rq[ri, c])
+
+
+PINS += [pin_bwd_dq_rows, pin_bwd_dq_rows_finite_differences]
+
 PINS += [pin_golden_window, pin_golden_varlen, pin_window_brute_force, pin_window_special_cases,
          pin_varlen_is_per_sequence_dense, pin_golden_decode_paged, pin_paged_decode_properties,
          pin_golden_blocksparse, pin_blocksparse_properties, pin_window_bwd_brute_force,
@@ -654,6 +698,10 @@ MUTANTS = {
                            "_, p, _ = head_probs(qh, kk, scale, causal)"),
     "bwd_window_left_only": ("_, p, _ = head_probs(qh, kk, scale, causal, window=window)",
                              "_, p, _ = head_probs(qh, kk, scale, causal, window=(window[0], -1))"),
+    "dq_rows_d_dropped": ("dsr = pr * (dpr - dr[:, None])", "dsr = pr * dpr"),
+    "dq_rows_wrong_kv_head": ("kv_head = h // _check_heads(hq, hkv)", "kv_head = h % hkv"),
+    "dq_rows_top_left_mask": ("head_probs(qr, kk, scale, causal, rows=rows, nq=q.shape[1])",
+                              "head_probs(qr, kk, scale, causal, rows=rows, nq=k.shape[1])"),
     "varlen_lse_row_major": ("lse[:, q0:q1] = lb[0]", "lse[:, q0:q1] = lb[0][::-1] if lb.shape[1] > 1 else lb[0]"),
 }
 

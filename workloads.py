@@ -33,6 +33,19 @@ def _randn(shape, gen, mult, dtype):
     return x.to(dtype)
 
 
+def device_normal(shape, seed, mult=1.0, dtype="bf16", device="cuda:0"):
+    """Standard normals drawn directly on a GPU from torch's seeded generator
+    (for inputs of several GiB, which drawing on the host and copying would
+    make slow), times ``mult``, rounded to the storage dtype. The same seed
+    gives the same bits on the same torch build and device type; a check
+    copies to the host only the slices it needs."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn(shape, generator=gen, dtype=torch.float32, device=device)
+    if mult != 1.0:
+        x.mul_(mult)
+    return x.to(DTYPES[dtype])
+
+
 def prefill_inputs(B, N, Hq, Hkv, d, dtype="bf16", seed=0, mult=1.0, with_do=False, Nk=None, do_mult=1.0):
     """Q [B, N, Hq, d], K and V [B, Nk, Hkv, d] (and dO like Q), drawn in that order.
     ``mult`` scales Q, K and V; ``do_mult`` scales dO."""
