@@ -141,6 +141,18 @@ def test_b1_n8192_h96_backward(hkv):
         assert_bf16_close(dq[:, :, sl], rdq, f"dQ heads {sl.start}..{sl.stop - 1}")
         assert_bf16_close(dk[:, :, kh:kh + 1], rdk, f"dK kv head {kh}")
         assert_bf16_close(dv[:, :, kh:kh + 1], rdv, f"dV kv head {kh}")
+    # Every query head: sampled dQ rows (row i of dQ needs only row i of P
+    # and dP, so the oracle's cost is linear in N per row).
+    rows = _sample_rows(w.N, np.random.default_rng(96 + hkv))
+    worst = 0.0
+    for h in range(w.Hq):
+        kh = h // g
+        rdq, _ = oracle.attn_bwd_dq_rows(f64(inp["q"][:, :, h:h + 1]), f64(inp["k"][:, :, kh:kh + 1]),
+                                         f64(inp["v"][:, :, kh:kh + 1]), f64(inp["do"][:, :, h:h + 1]), w.scale,
+                                         True, 0, 0, rows)
+        m, _ = assert_bf16_close(dq[0, rows, h], rdq, f"dQ rows head {h}")
+        worst = max(worst, m)
+    print(f"[parity] dQ: {w.Hq} heads x {len(rows)} rows, max error {worst:.3e}")
 
 
 @pytest.mark.timeout(600)
