@@ -403,6 +403,22 @@ def extras(fa_mod, lib, dev):
                           "fwd+bwd TFLOP/s": round(3.5 * 4 * d * pairs / ((ms_f + ms_b) * 1e9), 1),
                           "note": "fa_bwd: preprocess + dK/dV + dQ kernels"}
     del q, k, v, do, o, lse
+    # Causal fwd + bwd at head dim 64 (hidden 2048 = 32 heads x 64, 16k tokens).
+    pts = {}
+    for N in (2048, 16384):
+        B, H, d = 16384 // N, 32, 64
+        inp = workloads.prefill_inputs(B, N, H, H, d, "bf16", seed=7, mult=0.5, with_do=True)
+        q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+        del inp
+        o, lse = fa_mod.fa_fwd(q, k, v, causal=True)
+        pairs = _pairs_band(N, N, True) * B * H
+        tf_ = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=True, out=o, lse=lse))
+        tb_ = _time_ms(lambda: fa_mod.fa_bwd(q, k, v, o, do, lse, causal=True))
+        pts[f"N={N} B={B}"] = {"fwd": tf_, "bwd": tb_, "bwd_TFLOP/s": round(2.5 * 4 * d * pairs / (tb_["ms"] * 1e9), 1),
+                               "fwd+bwd TFLOP/s": round(3.5 * 4 * d * pairs / ((tf_["ms"] + tb_["ms"]) * 1e9), 1)}
+        del q, k, v, do, o, lse
+    out["fwd_bwd_d64_h2048"] = {"workload": "causal fwd + bwd, H=32 d=64, B*N = 16384 tokens", "points": pts,
+                                "note": "fa_bwd: preprocess + dK/dV + dQ kernels (d = 64 on the DMA kernels, 128-byte rows)"}
     # Sliding window at the GB200 timing shape, window of 4096 keys (causal).
     B, N, H, d = 1, 8192, 96, 128
     wl = 4095

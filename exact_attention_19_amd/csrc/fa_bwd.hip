@@ -99,426 +99,49 @@ __global__ __launch_bounds__(256) void bwd_dq_finalize_kernel(const float* __res
 }
 
 // ---------------------------------------------------------------------------
-// 2. dK, dV
-template <int D>
-struct DkdvSmem {
-  static constexpr int BQ = 64;
-  static constexpr int RS = D + 8;                 // padded row stride of Q and dO tiles
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = Q_OFF + BQ * RS;
-  static constexpr int QT_OFF = DO_OFF + BQ * RS;  // Q^T, 64 wide
-  static constexpr int DOT_OFF = QT_OFF + D * BQ;  // dO^T, 64 wide
-  static constexpr int STAGE_ELEMS = DOT_OFF + D * BQ;
-  static constexpr int STAGE_BYTES = STAGE_ELEMS * 2 + 2 * BQ * 4;  // + lse2, delta
-  static constexpr int BYTES = 2 * STAGE_BYTES;
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
-    float scale_log2) {
-  using SM = DkdvSmem<D>;
-  constexpr int BQ = SM::BQ;
-  constexpr int BKV = 128;
-  constexpr int DS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int C8 = D / 8;
-  constexpr int GROUPS = (BQ / 4) * C8;  // 4-row x 8-dim staging groups per tile
-  constexpr int G_PER_T = (GROUPS + kBwdThreads - 1) / kBwdThreads;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  const int BHK = B * Hkv;
-  const int bhk = blockIdx.x % BHK;
-  const int kt = blockIdx.x / BHK;  // low key tiles see the most query tiles: launched first
-  const int b = bhk / Hkv;
-  const int hk = bhk - b * Hkv;
-  const int G = Hq / Hkv;
-
-  const int64_t q_rs = (int64_t)Hq * D;
-  const int64_t kv_rs = (int64_t)Hkv * D;
-  const int k0 = kt * BKV;
-  const int kw0 = k0 + wave * 32;
-  const int my_key = kw0 + l32;
-  const bool wave_active = kw0 < N;
-
-  // Rows past N read row N-1 (their dK/dV are never written), so no load is
-  // predicated.
-  bf16x8 kf[DS], vf[DS];
-  {
-    const int64_t off = ((int64_t)b * N + min(my_key, N - 1)) * kv_rs + (int64_t)hk * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(k + off + 16 * s));
-      vf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(v + off + 16 * s));
-    }
-  }
-
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ) : 0;
-  const int per_head = nqt - qt0;
-  const int n_iter = G * per_head;
-
-  u32x4 qreg[G_PER_T][4], dreg[G_PER_T][4];
-  float lreg = 0.f, dlreg = 0.f;
-
-  auto load_tile = [&](int it) {
-    const int hq = hk * G + it / per_head;
-    const int q0 = (qt0 + it % per_head) * BQ;
-    const __bf16* qb = q + (int64_t)b * N * q_rs + (int64_t)hq * D;
-    const __bf16* db = dout + (int64_t)b * N * q_rs + (int64_t)hq * D;
-    // Query rows past N are read as row N-1; their LSE is set to +inf below,
-    // which makes their probabilities (and so their dS) exactly 0.
-#pragma unroll
-    for (int r = 0; r < G_PER_T; ++r) {
-      const int g = tid + r * kBwdThreads;
-      const int dc = g % C8, rg = g / C8;
-      if (GROUPS % kBwdThreads == 0 || g < GROUPS) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = min(q0 + rg * 4 + i, N - 1);
-          const int64_t off = (int64_t)row * q_rs + dc * 8;
-          qreg[r][i] = *reinterpret_cast<const u32x4*>(qb + off);
-          dreg[r][i] = *reinterpret_cast<const u32x4*>(db + off);
-        }
-      }
-    }
-    if (tid < BQ) {
-      const int row = q0 + tid;
-      // Rows past N get LSE = +inf, so their recomputed probabilities are 0.
-      lreg = row < N ? lse[((int64_t)b * Hq + hq) * N + row] * kLog2e : __builtin_inff();
-    } else if (tid < 2 * BQ) {
-      const int row = q0 + tid - BQ;
-      dlreg = row < N ? delta[((int64_t)b * Hq + hq) * N + row] : 0.f;
-    }
-  };
-
-  auto store_tile = [&](int stage) {
-    __bf16* base = reinterpret_cast<__bf16*>(smem_raw + stage * SM::STAGE_BYTES);
-    float* fl = reinterpret_cast<float*>(smem_raw + stage * SM::STAGE_BYTES + SM::STAGE_ELEMS * 2);
-#pragma unroll
-    for (int r = 0; r < G_PER_T; ++r) {
-      const int g = tid + r * kBwdThreads;
-      if (g < GROUPS) {
-        const int dc = g % C8, rg = g / C8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(base + SM::Q_OFF + (rg * 4 + i) * SM::RS + dc * 8) = qreg[r][i];
-          *reinterpret_cast<u32x4*>(base + SM::DO_OFF + (rg * 4 + i) * SM::RS + dc * 8) = dreg[r][i];
-        }
-        store_transposed_4x8(base + SM::QT_OFF, rg, dc, qreg[r]);
-        store_transposed_4x8(base + SM::DOT_OFF, rg, dc, dreg[r]);
-      }
-    }
-    if (tid < BQ) fl[tid] = lreg;
-    else if (tid < 2 * BQ) fl[tid] = dlreg;
-  };
-
-  f32x16 dkacc[DB], dvacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
-
-  if (n_iter > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < n_iter; ++it) {
-    const int stage = it & 1;
-    const bool has_next = it + 1 < n_iter;
-    if (has_next) load_tile(it + 1);
-
-    const int q0 = (qt0 + it % per_head) * BQ;
-    const bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
-    if (!skip) {
-      const __bf16* base = reinterpret_cast<const __bf16*>(smem_raw + stage * SM::STAGE_BYTES);
-      const float* lse2 = reinterpret_cast<const float*>(smem_raw + stage * SM::STAGE_BYTES + SM::STAGE_ELEMS * 2);
-      const float* dlt = lse2 + BQ;
-      const bool need_mask = (CAUSAL && q0 < kw0 + 31) || (kw0 + 32 > N);
-      bf16x8 pb[4], dsb[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        const __bf16* qrow = base + SM::Q_OFF + (qb * 32 + l32) * SM::RS + 8 * hh;
-        const __bf16* drow = base + SM::DO_OFF + (qb * 32 + l32) * SM::RS + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          sacc = mfma32(*reinterpret_cast<const bf16x8*>(qrow + 16 * s), kf[s], sacc);
-          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(drow + 16 * s), vf[s], dpacc);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qi = qb * 32 + 8 * j + 4 * hh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + qi);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt + qi);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = 4 * j + i;
-            float p = fast_exp2(sacc[e] * scale_log2 - l4[i]);
-            if (need_mask) {
-              const int query = q0 + qi + i;
-              const bool masked = (my_key >= N) || (CAUSAL && my_key > query);
-              p = masked ? 0.f : p;
-            }
-            const float ds = p * (dpacc[e] - d4[i]);
-            pb[qb * 2 + (e >> 3)][e & 7] = (__bf16)p;
-            dsb[qb * 2 + (e >> 3)][e & 7] = (__bf16)ds;
-          }
-        }
-      }
-#pragma unroll
-      for (int dbk = 0; dbk < DB; ++dbk) {
-        const int d = dbk * 32 + l32;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          dvacc[dbk] = mfma32(load_tr_operand(base + SM::DOT_OFF, d, st, hh), pb[st], dvacc[dbk]);
-          dkacc[dbk] = mfma32(load_tr_operand(base + SM::QT_OFF, d, st, hh), dsb[st], dkacc[dbk]);
-        }
-      }
-    }
-
-    if (has_next) store_tile(stage ^ 1);
-    __syncthreads();
-  }
-
-  if (!wave_active || my_key >= N) return;
-  const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
-#pragma unroll
-  for (int dbk = 0; dbk < DB; ++dbk) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = dbk * 32 + 8 * j + 4 * hh;
-      u32x2 wk, wv;
-      wk[0] = pack_bf16x2(dkacc[dbk][4 * j + 0] * scale, dkacc[dbk][4 * j + 1] * scale);
-      wk[1] = pack_bf16x2(dkacc[dbk][4 * j + 2] * scale, dkacc[dbk][4 * j + 3] * scale);
-      wv[0] = pack_bf16x2(dvacc[dbk][4 * j + 0], dvacc[dbk][4 * j + 1]);
-      wv[1] = pack_bf16x2(dvacc[dbk][4 * j + 2], dvacc[dbk][4 * j + 3]);
-      *reinterpret_cast<u32x2*>(dk + off + d) = wk;
-      *reinterpret_cast<u32x2*>(dv + off + d) = wv;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// 3. dQ
-template <int D>
-struct DqSmem {
-  static constexpr int BN = 64;
-  static constexpr int RS = D + 8;
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = K_OFF + BN * RS;
-  static constexpr int KT_OFF = V_OFF + BN * RS;  // K^T, 64 wide
-  static constexpr int STAGE_ELEMS = KT_OFF + D * BN;
-  static constexpr int BYTES = 2 * STAGE_ELEMS * 2;
-};
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
-    __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles) {
-  using SM = DqSmem<D>;
-  constexpr int BN = SM::BN;
-  constexpr int BM = 128;
-  constexpr int DS = D / 16;
-  constexpr int DB = D / 32;
-  constexpr int C8 = D / 8;
-  constexpr int GROUPS = (BN / 4) * C8;
-  constexpr int G_PER_T = (GROUPS + kBwdThreads - 1) / kBwdThreads;
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-
-  const int BH = B * Hq;
-  const int bh = blockIdx.x % BH;
-  const int rank = blockIdx.x / BH;
-  const int qt = CAUSAL ? (num_q_tiles - 1 - rank) : rank;
-  const int b = bh / Hq;
-  const int hq = bh - b * Hq;
-  const int hk = hq / (Hq / Hkv);
-
-  const int64_t q_rs = (int64_t)Hq * D;
-  const int64_t kv_rs = (int64_t)Hkv * D;
-  const int q0 = qt * BM;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
-  const bool wave_active = qw0 < N;
-
-  // Rows past N read row N-1 (their dQ is never written).
-  bf16x8 qf[DS], dof[DS];
-  float my_lse2, my_dlt;
-  {
-    const int row = min(my_q, N - 1);
-    const int64_t off = ((int64_t)b * N + row) * q_rs + (int64_t)hq * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      qf[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(q + off + 16 * s));
-      dof[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(dout + off + 16 * s));
-    }
-    my_lse2 = lse[((int64_t)b * Hq + hq) * N + row] * kLog2e;
-    my_dlt = delta[((int64_t)b * Hq + hq) * N + row];
-  }
-
-  int kv_end = N;
-  if (CAUSAL) kv_end = min(N, q0 + BM);
-  const int n_tiles = (kv_end + BN - 1) / BN;
-  const __bf16* kb = k + (int64_t)b * N * kv_rs + (int64_t)hk * D;
-  const __bf16* vb = v + (int64_t)b * N * kv_rs + (int64_t)hk * D;
-
-  u32x4 kreg[G_PER_T][4], vreg[G_PER_T][4];
-  auto load_tile = [&](int t) {
-    const int k0 = t * BN;
-    // Key rows past N are read as row N-1; their probabilities are masked to 0.
-#pragma unroll
-    for (int r = 0; r < G_PER_T; ++r) {
-      const int g = tid + r * kBwdThreads;
-      const int dc = g % C8, kg = g / C8;
-      if (GROUPS % kBwdThreads == 0 || g < GROUPS) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(k0 + kg * 4 + i, N - 1);
-          const int64_t off = (int64_t)key * kv_rs + dc * 8;
-          kreg[r][i] = *reinterpret_cast<const u32x4*>(kb + off);
-          vreg[r][i] = *reinterpret_cast<const u32x4*>(vb + off);
-        }
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    __bf16* base = smem + stage * SM::STAGE_ELEMS;
-#pragma unroll
-    for (int r = 0; r < G_PER_T; ++r) {
-      const int g = tid + r * kBwdThreads;
-      if (g < GROUPS) {
-        const int dc = g % C8, kg = g / C8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<u32x4*>(base + SM::K_OFF + (kg * 4 + i) * SM::RS + dc * 8) = kreg[r][i];
-          *reinterpret_cast<u32x4*>(base + SM::V_OFF + (kg * 4 + i) * SM::RS + dc * 8) = vreg[r][i];
-        }
-        store_transposed_4x8(base + SM::KT_OFF, kg, dc, kreg[r]);
-      }
-    }
-  };
-
-  f32x16 dqacc[DB];
-#pragma unroll
-  for (int i = 0; i < DB; ++i) dqacc[i] = f32x16{};
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(t + 1);
-    const int k0 = t * BN;
-    const bool skip = !wave_active || (CAUSAL && k0 > qw0 + 31);
-    if (!skip) {
-      const __bf16* base = smem + stage * SM::STAGE_ELEMS;
-      const bool need_mask = (CAUSAL && (k0 + BN - 1 > qw0)) || (k0 + BN > N);
-      bf16x8 dsb[4];
-#pragma unroll
-      for (int kbk = 0; kbk < 2; ++kbk) {
-        f32x16 sacc = f32x16{}, dpacc = f32x16{};
-        const __bf16* krow = base + SM::K_OFF + (kbk * 32 + l32) * SM::RS + 8 * hh;
-        const __bf16* vrow = base + SM::V_OFF + (kbk * 32 + l32) * SM::RS + 8 * hh;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * s), qf[s], sacc);
-          dpacc = mfma32(*reinterpret_cast<const bf16x8*>(vrow + 16 * s), dof[s], dpacc);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float p = fast_exp2(sacc[e] * scale_log2 - my_lse2);
-          if (need_mask) {
-            const int key = k0 + kbk * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-            const bool masked = (key >= N) || (CAUSAL && key > my_q);
-            p = masked ? 0.f : p;
-          }
-          dsb[kbk * 2 + (e >> 3)][e & 7] = (__bf16)(p * (dpacc[e] - my_dlt));
-        }
-      }
-#pragma unroll
-      for (int dbk = 0; dbk < DB; ++dbk) {
-        const int d = dbk * 32 + l32;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          dqacc[dbk] = mfma32(load_tr_operand(base + SM::KT_OFF, d, st, hh), dsb[st], dqacc[dbk]);
-        }
-      }
-    }
-    if (has_next) store_tile(stage ^ 1);
-    __syncthreads();
-  }
-
-  if (!wave_active || my_q >= N) return;
-  __bf16* orow = dq + ((int64_t)b * N + my_q) * q_rs + (int64_t)hq * D;
-#pragma unroll
-  for (int dbk = 0; dbk < DB; ++dbk) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x2 w;
-      w[0] = pack_bf16x2(dqacc[dbk][4 * j + 0] * scale, dqacc[dbk][4 * j + 1] * scale);
-      w[1] = pack_bf16x2(dqacc[dbk][4 * j + 2] * scale, dqacc[dbk][4 * j + 3] * scale);
-      *reinterpret_cast<u32x2*>(orow + dbk * 32 + 8 * j + 4 * hh) = w;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// d = 128 kernels. Row-major 64 x 128 tiles go from global memory straight
-// into XOR-swizzled LDS (global_load_lds_dwordx4); transposed MFMA operands
-// (Q^T, dO^T, K^T) are read from the same tiles with ds_read_b64_tr_b16, so
-// no tile is stored twice and nothing passes through staging registers.
+// 2. dK, dV and 3. dQ. Row-major 64 x d tiles (rows of 2 d bytes, swizzled by
+// row_swz) go from global memory straight into LDS (global_load_lds_dwordx4);
+// transposed MFMA operands (Q^T, dO^T, K^T) are read from the same tiles with
+// ds_read_b64_tr_b16, so no tile is stored twice and nothing passes through
+// staging registers.
 // For a 16-row step st of a 64-row tile, a transposed read at row offset
 // 4*hh + j/4 (+8) yields, for the lane's column, the rows the score
 // accumulator pairs with it: 16*st + 4*hh + {0..3} and 16*st + 8 + 4*hh + {0..3}.
 
 // Per-lane byte offsets inside a swizzled tile for a transposed operand read
 // (second read at index 1), for column block 0; column block db is reached by
-// XOR with 64*db, 16-row step st by adding 4096*st.
+// XOR with 64*db, 16-row step st by adding 16 rows (32*D bytes) per step.
+template <int D = 128>
 __device__ __forceinline__ void tr_offsets(int lane, int (&off)[2]) {
   const int j = lane & 15, g = lane >> 4, hh = lane >> 5;
 #pragma unroll
   for (int rd = 0; rd < 2; ++rd) {
     const int r = 4 * hh + (j >> 2) + 8 * rd;
     const int unit = 2 * (g & 1) + ((j & 3) >> 1);
-    off[rd] = r * 256 + 16 * (unit ^ tile_swz(r)) + 8 * (j & 1);
+    off[rd] = r * 2 * D + 16 * (unit ^ row_swz<D>(r)) + 8 * (j & 1);
   }
 }
 
+template <int D = 128>
 __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, int st, int db, const int (&off)[2]) {
-  const i16x4 lo = tr_read(tile + st * 4096 + (off[0] ^ (64 * db)));
-  const i16x4 hi = tr_read(tile + st * 4096 + (off[1] ^ (64 * db)));
+  const i16x4 lo = tr_read(tile + st * 32 * D + (off[0] ^ (64 * db)));
+  const i16x4 hi = tr_read(tile + st * 32 * D + (off[1] ^ (64 * db)));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Row operand (16 bytes of row r0 + l32, 16-deep step s) from a swizzled
 // tile: byte offset (roff ^ (32*s)) + 8192 * (r0 / 32), roff from row_offset.
+template <int D = 128>
 __device__ __forceinline__ int row_offset(int lane) {
   const int l32 = lane & 31, hh = lane >> 5;
-  return l32 * 256 + 16 * (hh ^ tile_swz(l32));
+  return l32 * 2 * D + 16 * (hh ^ row_swz<D>(l32));
 }
 
-// dK, dV for d = 128: one workgroup per (b, kv head, 128 keys); wave w keeps
+// dK, dV (d = 128 or 64): one workgroup per (b, kv head, 128 keys); wave w keeps
 // keys k0 + 32w .. +31 (K, V fragments and dK^T, dV^T accumulators in
 // registers) and sweeps the visible 64-row query tiles of every query head
-// in the GQA group.
+// in the GQA group. At d = 64 the fragments and accumulators take half the
+// registers (248 in all), so two workgroups share a CU; at d = 128 one does.
 //
 // FUSED (the atomic backward) also produces dQ, so that the backward runs
 // the five N x N x d products once each instead of recomputing S and dP in a
@@ -527,21 +150,24 @@ __device__ __forceinline__ int row_offset(int lane) {
 // dQ[:, 32w .. 32w+31] += dS K over the workgroup's 128 keys (K kept in LDS)
 // into an fp32 accumulator with atomic adds (so dQ's last bits depend on the
 // order in which workgroups arrive).
-template <bool CAUSAL, bool WINDOW, int BQ, bool FUSED = false>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
+template <bool CAUSAL, bool WINDOW, int BQ, bool FUSED = false, int D = 128>
+__global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
     float scale_log2, int win_left, int win_right, float* __restrict__ dq_acc) {
-  constexpr int D = 128, DS = 8, DB = 4, BKV = 128;
+  constexpr int DS = D / 16, DB = D / 32, BKV = 128;
+  constexpr int ROWB = 2 * D;                  // bytes of one tile row
+  constexpr int QBLK = 32 * ROWB;              // 32 rows of a tile
   constexpr int NQB = BQ / 32;                 // 32-query blocks per query tile
   static_assert(BQ == 64 || BQ == 128, "query tiles of 64 or 128 rows");
+  static_assert(D == 128 || (D == 64 && !FUSED), "d = 128, or d = 64 without the fused dQ");
   static_assert(!FUSED || (BQ == 64 && !WINDOW), "fused dQ: 64-query tiles, no window");
   // Key j is visible to query i iff j <= i (causal), i - wl <= j <= i + wr
   // (window, a negative side unbounded) and both are < N.
   const int wl = WINDOW ? win_left : -1;
   const int wr = WINDOW ? win_right : -1;
-  constexpr int TILE = BQ * 256;               // one BQ x 128 bf16 tile (Q, then dO)
+  constexpr int TILE = BQ * ROWB;              // one BQ x D bf16 tile (Q, then dO)
   constexpr int VEC_OFF = 2 * TILE;            // lse2 (BQ floats) then delta (BQ floats)
   constexpr int STAGE = 2 * TILE + 8 * BQ;
   constexpr int KT_OFF = 2 * STAGE;            // FUSED: the workgroup's 128 K rows (two 64-row tiles)
@@ -626,11 +252,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   };
   Cursor cur{0, 0};
 
-  const int roff = row_offset(lane);
+  const int roff = row_offset<D>(lane);
   int toff[2];
-  tr_offsets(lane, toff);
+  tr_offsets<D>(lane, toff);
   const uint32_t q_rs_bytes = (uint32_t)(q_rs * 2);
-  const uint32_t dma_off = dma_lane_offset(lane, wave, q_rs_bytes);
+  const uint32_t dma_off = dma_lane_offset_d<D>(lane, wave, q_rs_bytes);
+  constexpr int CPW = 64 * ROWB / 1024 / 4;  // 1 KB chunks per wave of a 64-row tile
 
   f32x16 dkacc[DB], dvacc[DB];
 #pragma unroll
@@ -643,10 +270,10 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 #pragma unroll
     for (int h = 0; h < BQ / 64; ++h) {
       const int64_t off = ((int64_t)b * N + q0 + 64 * h) * q_rs * 2 + (int64_t)hq * D * 2;
-      dma_rows64(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0 - 64 * h, st + h * 16384, wave,
-                 4, 4, dma_off);
-      dma_rows64(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0 - 64 * h,
-                 st + TILE + h * 16384, wave, 4, 4, dma_off);
+      dma_rows64_d<D>(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0 - 64 * h,
+                      st + h * 64 * ROWB, wave, 4, CPW, dma_off);
+      dma_rows64_d<D>(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0 - 64 * h,
+                      st + TILE + h * 64 * ROWB, wave, 4, CPW, dma_off);
     }
     const int64_t vb = ((int64_t)b * Hq + hq) * N;
     // lse2 then delta, 64 floats per wave instruction, spread over the waves
@@ -672,8 +299,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
     Scores r{f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      r.s = mfma32(*reinterpret_cast<const bf16x8*>(qs + qb * 8192 + (roff ^ (32 * s))), kf[s], r.s);
-      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + qb * 8192 + (roff ^ (32 * s))), vf[s], r.dp);
+      r.s = mfma32(*reinterpret_cast<const bf16x8*>(qs + qb * QBLK + (roff ^ (32 * s))), kf[s], r.s);
+      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + qb * QBLK + (roff ^ (32 * s))), vf[s], r.dp);
     }
     return r;
   };
@@ -719,8 +346,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
         const int stp = 2 * qb + tt;
-        dvacc[db] = mfma32(tr_operand(ds_, stp, db, toff), pr.p[tt], dvacc[db]);
-        dkacc[db] = mfma32(tr_operand(qs, stp, db, toff), pr.ds[tt], dkacc[db]);
+        dvacc[db] = mfma32(tr_operand<D>(ds_, stp, db, toff), pr.p[tt], dvacc[db]);
+        dkacc[db] = mfma32(tr_operand<D>(qs, stp, db, toff), pr.ds[tt], dkacc[db]);
       }
     }
   };
@@ -877,16 +504,19 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkdv_d128_kernel(
   }
 }
 
-// dQ for d = 128: one workgroup per (b, query head, 128 query rows), shaped
-// like the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
-template <bool CAUSAL, bool WINDOW>
+// dQ (d = 128 or 64): one workgroup per (b, query head, 128 query rows),
+// shaped like the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
+template <bool CAUSAL, bool WINDOW, int D = 128>
 __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
     __bf16* __restrict__ dq, int B, int Hq, int Hkv, int N, float scale, float scale_log2, int num_q_tiles,
     int win_left, int win_right) {
-  constexpr int D = 128, DS = 8, DB = 4, BM = 128, BN = 64;
-  constexpr int TILE = 64 * 256;
+  constexpr int DS = D / 16, DB = D / 32, BM = 128, BN = 64;
+  constexpr int ROWB = 2 * D;                  // bytes of one tile row
+  constexpr int KBLK = 32 * ROWB;              // 32 rows of a tile
+  constexpr int TILE = 64 * ROWB;
+  static_assert(D == 64 || D == 128, "d = 64 or 128");
   constexpr int STAGE = 2 * TILE;  // K tile then V tile
   extern __shared__ __align__(1024) unsigned char smem[];
 
@@ -952,11 +582,12 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v + (int64_t)b * N * kv_rs + (int64_t)hk * D);
   const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
-  const uint32_t dma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
+  const uint32_t dma_off = dma_lane_offset_d<D>(lane, wave, kv_rs_bytes);
+  constexpr int CPW = TILE / 1024 / 4;  // 1 KB chunks per wave of a tile
 
-  const int roff = row_offset(lane);
+  const int roff = row_offset<D>(lane);
   int toff[2];
-  tr_offsets(lane, toff);
+  tr_offsets<D>(lane, toff);
 
   f32x16 dqacc[DB];
 #pragma unroll
@@ -965,8 +596,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
   auto issue = [&](int t, int stage) __attribute__((always_inline)) {
     unsigned char* st = smem + stage * STAGE;
     const int64_t off = (int64_t)t * BN * kv_rs * 2;
-    dma_rows64(kbase + off, kv_rs_bytes, N - t * BN, st, wave, 4, 4, dma_off);
-    dma_rows64(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, 4, dma_off);
+    dma_rows64_d<D>(kbase + off, kv_rs_bytes, N - t * BN, st, wave, 4, CPW, dma_off);
+    dma_rows64_d<D>(vbase + off, kv_rs_bytes, N - t * BN, st + TILE, wave, 4, CPW, dma_off);
   };
 
   // Same skew as the dK/dV kernel: scores of key block 1 beside the algebra
@@ -978,8 +609,8 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     Scores r{f32x16{}, f32x16{}};
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      r.s = mfma32(*reinterpret_cast<const bf16x8*>(ks + kbk * 8192 + (roff ^ (32 * s))), qf[s], r.s);
-      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(vs + kbk * 8192 + (roff ^ (32 * s))), dof[s], r.dp);
+      r.s = mfma32(*reinterpret_cast<const bf16x8*>(ks + kbk * KBLK + (roff ^ (32 * s))), qf[s], r.s);
+      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(vs + kbk * KBLK + (roff ^ (32 * s))), dof[s], r.dp);
     }
     return r;
   };
@@ -1017,7 +648,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        dqacc[db] = mfma32(tr_operand(st, 2 * kbk + tt, db, toff), d.v[tt], dqacc[db]);
+        dqacc[db] = mfma32(tr_operand<D>(st, 2 * kbk + tt, db, toff), d.v[tt], dqacc[db]);
       }
     }
   };
@@ -1037,7 +668,7 @@ __global__ __launch_bounds__(kBwdThreads, 2) void bwd_dq_d128_kernel(
     update(st, 0, d0);
     const DsB d1 = algebra(s1);
     update(st, 1, d1);
-    if constexpr (!MASK) {
+    if constexpr (!MASK && D == 128) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -1159,11 +790,11 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
         return hipGetLastError();
       }
     }
-    if (D == 128) {
+    {
       constexpr int BQ = kDkdvQueryTile;
-      auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>;
-      constexpr size_t smem = 2 * (2 * BQ * 256 + 8 * BQ);
-      hipError_t e = set_smem_once<bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ>>(smem);
+      auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ, false, D>;
+      constexpr size_t smem = 2 * (2 * BQ * 2 * D + 8 * BQ);
+      hipError_t e = set_smem_once<bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ, false, D>>(smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                          (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1171,14 +802,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
                          scale_log2, a.win_left, a.win_right, nullptr);
       return hipGetLastError();
     }
-    auto kern = bwd_dkdv_kernel<D, CAUSAL>;
-    hipError_t e = set_smem_once<bwd_dkdv_kernel<D, CAUSAL>>(DkdvSmem<D>::BYTES);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DkdvSmem<D>::BYTES, a.stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                       (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
-                       scale_log2);
-    return hipGetLastError();
   }
   if (a.dq_acc) {  // atomic backward: dQ = bf16(scale * dQacc)
     const int64_t n8 = (int64_t)a.B * a.N * a.Hq * D / 8;
@@ -1191,10 +814,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
   const int nqt = (a.N + 127) / 128;
   const int64_t grid = (int64_t)nqt * a.B * a.Hq;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (D == 128) {
-    auto kern = bwd_dq_d128_kernel<CAUSAL, WINDOW>;
-    constexpr size_t smem = 2 * 2 * 64 * 256;
-    hipError_t e = set_smem_once<bwd_dq_d128_kernel<CAUSAL, WINDOW>>(smem);
+  {
+    auto kern = bwd_dq_d128_kernel<CAUSAL, WINDOW, D>;
+    constexpr size_t smem = 2 * 2 * 64 * 2 * D;
+    hipError_t e = set_smem_once<bwd_dq_d128_kernel<CAUSAL, WINDOW, D>>(smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,
                        (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
@@ -1202,13 +825,6 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
                        a.win_left, a.win_right);
     return hipGetLastError();
   }
-  auto kern = bwd_dq_kernel<D, CAUSAL>;
-  hipError_t e = set_smem_once<bwd_dq_kernel<D, CAUSAL>>(DqSmem<D>::BYTES);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), DqSmem<D>::BYTES, a.stream,
-                     (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, a.lse,
-                     (const float*)delta, (__bf16*)a.dq, a.B, a.Hq, a.Hkv, a.N, a.scale, scale_log2, nqt);
-  return hipGetLastError();
 }
 
 }  // namespace
