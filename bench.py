@@ -303,6 +303,19 @@ def _time_ms(fn, reps=None, warm=5):
             "reps": reps}
 
 
+def _fwd_roofline(flops, B, N, Hq, Hkv, d, ms):
+    """Where a forward point sits on the roofline: its minimum HBM bytes (Q, K,
+    V read once, O and the fp32 LSE written once), the rate that makes, and
+    which of the two bounds (bf16 MFMA peak, HBM peak) is the larger time; the
+    fraction is that bound's time over the measured time."""
+    nbytes = 2 * B * N * d * (2 * Hq + 2 * Hkv) + 4 * B * Hq * N
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "hbm" if t_hbm > t_mfma else "mfma"
+    return {"min_bytes": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bound": bound,
+            "roofline_frac": round(max(t_mfma, t_hbm) / (ms * 1e-3), 4)}
+
+
 def _pairs_band(nq, nk, causal, wl=-1, wr=-1):
     """Visible (query, key) pairs of one head: keys j with i + off - wl <= j <=
     i + off + wr (and j <= i + off when causal), off = nk - nq."""
@@ -343,7 +356,8 @@ def extras(fa_mod, lib, dev):
         t = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=True, out=o_, lse=l_))
         pairs = _pairs_band(N, N, True) * B * 16
         tf = 4 * 128 * pairs / (t["ms"] * 1e9)
-        sweep[f"N={N} B={B}"] = {**t, "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        sweep[f"N={N} B={B}"] = {**t, "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                 **_fwd_roofline(4 * 128 * pairs, B, N, 16, 16, 128, t["ms"])}
         del o_, l_
         del q, k, v
     out["fwd_sweep_h2048"] = {"workload": "causal forward, H=16 d=128, B*N = 16384 tokens", "points": sweep}
@@ -359,8 +373,9 @@ def extras(fa_mod, lib, dev):
             t = _time_ms(lambda: fa_mod.fa_fwd(q, k, v, causal=causal, out=o_, lse=l_))
             pairs = _pairs_band(N, N, causal) * B * 32
             tf = 4 * 64 * pairs / (t["ms"] * 1e9)
-            sweep[f"N={N} B={B}{' causal' if causal else ''}"] = {**t, "TFLOP/s": round(tf, 1),
-                                                                  "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            sweep[f"N={N} B={B}{' causal' if causal else ''}"] = {
+                **t, "TFLOP/s": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                **_fwd_roofline(4 * 64 * pairs, B, N, 32, 32, 64, t["ms"])}
             del o_, l_
             del q, k, v
     out["fwd_sweep_h2048_d64"] = {"workload": "forward, H=32 d=64, B*N = 16384 tokens", "points": sweep}

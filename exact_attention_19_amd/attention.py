@@ -69,7 +69,7 @@ def fa_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
 
 
 def fa_fwd_window(q, k, v, window, scale=None, causal=False, out=None, lse=None):
-    """Sliding-window forward (bf16, d = 128): window = (left, right), -1 is
+    """Sliding-window forward (bf16, d = 64 or 128): window = (left, right), -1 is
     unbounded on that side. Returns (o, lse) laid out as fa_fwd, written into
     out / lse when given."""
     _check_tensor("q", q, torch.bfloat16, 4)
@@ -95,7 +95,7 @@ def fa_fwd_window(q, k, v, window, scale=None, causal=False, out=None, lse=None)
 
 def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None, causal=False,
                   window=(-1, -1)):
-    """Forward over packed variable-length sequences (bf16, d = 128).
+    """Forward over packed variable-length sequences (bf16, d = 64 or 128).
 
     q [total_q, Hq, d], k/v [total_k, Hkv, d]; cu_seqlens_q/k: int32 [B + 1]
     device prefix sums. Returns (o [total_q, Hq, d], lse [Hq, total_q])."""
@@ -124,7 +124,7 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
 
 
 def fa_fwd_blocksparse(q, k, v, block_mask, scale=None, causal=False):
-    """Block-sparse forward (bf16, d = 128): block_mask is a uint8 device tensor
+    """Block-sparse forward (bf16, d = 64 or 128): block_mask is a uint8 device tensor
     of [nb, nb] (shared) or [B, Hq, nb, nb] bytes, nb = ceil(N / 128).
     Returns (o, lse) laid out as fa_fwd."""
     _check_tensor("q", q, torch.bfloat16, 4)
@@ -154,7 +154,7 @@ def fa_bwd(q, k, v, o, dout, lse, scale=None, causal=False, window=(-1, -1), dq=
            deterministic=True):
     """Attention backward from the forward's O and LSE. Returns (dq, dk, dv),
     written into the given tensors when passed. A window other than (-1, -1)
-    calls fa_bwd_window (d = 128); deterministic=False calls fa_bwd_atomic
+    calls fa_bwd_window (d = 64 or 128); deterministic=False calls fa_bwd_atomic
     (d = 128, no window: dQ accumulated with fp32 atomics)."""
     _check_tensor("q", q, torch.bfloat16, 4)
     dev = q.device

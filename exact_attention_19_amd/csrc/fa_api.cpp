@@ -106,8 +106,6 @@ fa_status bwd_common(const char* fn, int stage, const void* q, const void* k, co
   if (atomic && d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: the atomic backward needs d = 128 (got %d)", fn, d);
   if (window_left < -1 || window_right < -1)
     return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
-  if ((window_left >= 0 || window_right >= 0) && d != 128)
-    return fail(FA_ERR_UNSUPPORTED, "%s: a window needs d = 128 (got %d)", fn, d);
   const bool all = stage < 0;
   if (all || stage == 0) {
     FA_TRY(check_ptr(fn, "o", o, 16));
@@ -207,7 +205,6 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
     return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
   if (window_left < 0 && window_right < 0) return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, dtype, stream);
   if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 supports a window", fn);
-  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: a window needs d = 128 (got %d)", fn, d);
   FA_TRY(check_ptr(fn, "q", q, 16));
   FA_TRY(check_ptr(fn, "k", k, 16));
   FA_TRY(check_ptr(fn, "v", v, 16));
@@ -232,7 +229,6 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   if (window_left < -1 || window_right < -1)
     return fail(FA_ERR_INVALID_ARG, "%s: window (%d, %d): each side must be >= -1", fn, window_left, window_right);
   if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is supported", fn);
-  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: d = 128 only (got %d)", fn, d);
   FA_TRY(check_ptr(fn, "q", q, 16));
   FA_TRY(check_ptr(fn, "k", k, 16));
   FA_TRY(check_ptr(fn, "v", v, 16));
@@ -261,7 +257,6 @@ fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* 
   static const char* fn = "fa_fwd_blocksparse";
   FA_TRY(check_sizes(fn, B, Hq, Hkv, N, d, scale));
   if (dtype != FA_BF16) return fail(FA_ERR_UNSUPPORTED, "%s: only bf16 is supported", fn);
-  if (d != 128) return fail(FA_ERR_UNSUPPORTED, "%s: d = 128 only (got %d)", fn, d);
   const int nb = (N + fa::kBlockSparseBlock - 1) / fa::kBlockSparseBlock;
   if (nb > fa::kBlockSparseMaxBlocks)
     return fail(FA_ERR_UNSUPPORTED, "%s: N = %d exceeds %d", fn, N, fa::kBlockSparseMaxBlocks * fa::kBlockSparseBlock);

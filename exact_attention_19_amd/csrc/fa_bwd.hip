@@ -830,8 +830,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
 }  // namespace
 
 hipError_t launch_bwd_stage(const BwdArgs& a, float* delta, int stage) {
-  if (a.d == 64) return a.causal ? launch_bwd_t<64, true>(a, delta, stage) : launch_bwd_t<64, false>(a, delta, stage);
-  if (a.win_left >= 0 || a.win_right >= 0) {
+  const bool window = a.win_left >= 0 || a.win_right >= 0;
+  if (a.d == 64) {
+    if (window)
+      return a.causal ? launch_bwd_t<64, true, true>(a, delta, stage) : launch_bwd_t<64, false, true>(a, delta, stage);
+    return a.causal ? launch_bwd_t<64, true>(a, delta, stage) : launch_bwd_t<64, false>(a, delta, stage);
+  }
+  if (window) {
     return a.causal ? launch_bwd_t<128, true, true>(a, delta, stage) : launch_bwd_t<128, false, true>(a, delta, stage);
   }
   return a.causal ? launch_bwd_t<128, true>(a, delta, stage) : launch_bwd_t<128, false>(a, delta, stage);

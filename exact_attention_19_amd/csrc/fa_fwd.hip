@@ -284,7 +284,7 @@ __global__ __launch_bounds__(NWAVES * 64, (QB == 1 ? (D == 64 ? 3 * 4 : 8) : 4) 
   constexpr bool VARLEN = (MODE & kModeVarlen) != 0;
   constexpr bool WINDOW = (MODE & kModeWindow) != 0;
   constexpr bool BSPARSE = (MODE & kModeBlockSparse) != 0;
-  static_assert(D == 128 || (D == 64 && MODE == 0 && QB == 1), "d = 64: dense batches, one query block per wave");
+  static_assert(D == 128 || (D == 64 && QB == 1), "d = 64: one query block per wave");
   constexpr int ROWB = 2 * D;           // bytes of one tile row
   constexpr int WQ = 32 * QB;           // query rows per wave
   constexpr int BM = NWAVES * WQ;       // query rows per workgroup
@@ -923,26 +923,23 @@ hipError_t launch_fwd(const FwdArgs& a) {
   return a.causal ? launch_d128<4, 2, 1, true>(a) : launch_d128<4, 2, 1, false>(a);
 }
 
-hipError_t launch_fwd_blocksparse(const FwdArgs& a, const FwdSeq& seq) {
-  return a.causal ? launch_d128<4, 2, 1, true, kModeBlockSparse>(a, seq)
-                  : launch_d128<4, 2, 1, false, kModeBlockSparse>(a, seq);
+// The masked modes (block-sparse, varlen, window) run the DMA kernel at
+// either head dim (at d = 64 with 128-byte rows, as dense batches of many
+// workgroups do).
+template <int MODE>
+hipError_t launch_mode(const FwdArgs& a, const FwdSeq& seq) {
+  if (a.d == 64) return a.causal ? launch_d128<4, 2, 1, true, MODE, 64>(a, seq) : launch_d128<4, 2, 1, false, MODE, 64>(a, seq);
+  return a.causal ? launch_d128<4, 2, 1, true, MODE>(a, seq) : launch_d128<4, 2, 1, false, MODE>(a, seq);
 }
+
+hipError_t launch_fwd_blocksparse(const FwdArgs& a, const FwdSeq& seq) { return launch_mode<kModeBlockSparse>(a, seq); }
 
 hipError_t launch_fwd_seq(const FwdArgs& a, const FwdSeq& seq) {
   const bool varlen = seq.cu_q != nullptr;
   const bool window = seq.win_left >= 0 || seq.win_right >= 0;
-  if (varlen && window) {
-    return a.causal ? launch_d128<4, 2, 1, true, kModeVarlen | kModeWindow>(a, seq)
-                    : launch_d128<4, 2, 1, false, kModeVarlen | kModeWindow>(a, seq);
-  }
-  if (varlen) {
-    return a.causal ? launch_d128<4, 2, 1, true, kModeVarlen>(a, seq)
-                    : launch_d128<4, 2, 1, false, kModeVarlen>(a, seq);
-  }
-  if (window) {
-    return a.causal ? launch_d128<4, 2, 1, true, kModeWindow>(a, seq)
-                    : launch_d128<4, 2, 1, false, kModeWindow>(a, seq);
-  }
+  if (varlen && window) return launch_mode<kModeVarlen | kModeWindow>(a, seq);
+  if (varlen) return launch_mode<kModeVarlen>(a, seq);
+  if (window) return launch_mode<kModeWindow>(a, seq);
   return launch_fwd(a);
 }
 

@@ -81,7 +81,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
  * fa_fwd. Layouts, alignment and outputs as fa_fwd.
  * A row that sees no key has O = 0 and LSE = -inf.
  * Errors: FA_ERR_INVALID_ARG as fa_fwd, or a window side < -1;
- *   FA_ERR_UNSUPPORTED for a window with dtype != FA_BF16 or d != 128.
+ *   FA_ERR_UNSUPPORTED for a window with dtype != FA_BF16 (d = 64 or 128).
  */
 fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Hq, int Hkv, int N, int d, float scale, int causal,
@@ -108,10 +108,10 @@ fa_status fa_fwd_window(const void* q, const void* k, const void* v, void* o, fl
  *   a longer sequence past max_seqlen_q are left unwritten. Prefix sums are
  *   read on the device and clamped to [0, total], so malformed values cannot
  *   cause accesses outside the tensors (their results are unspecified).
- * Only d = 128 and FA_BF16. Pointers 16-byte aligned (lse, cu_*: 4-byte).
+ * d = 64 or 128, FA_BF16 only. Pointers 16-byte aligned (lse, cu_*: 4-byte).
  * Errors: FA_ERR_INVALID_ARG for NULL/misaligned pointers, B, Hq, Hkv,
  *   max_seqlen_q or total_q <= 0, total_k < 0, Hq % Hkv != 0, a bad scale or a
- *   window side < -1; FA_ERR_UNSUPPORTED for d != 128 or dtype != FA_BF16.
+ *   window side < -1; FA_ERR_UNSUPPORTED for d not 64 or 128, or dtype != FA_BF16.
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -129,7 +129,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
  * like masked ones; causal = 1 applies the causal mask as well. A row that
  * keeps no key has O = 0, LSE = -inf. Skipped blocks cost neither loads nor
  * arithmetic. Layouts, alignment and outputs as fa_fwd.
- * Errors: as fa_fwd, plus FA_ERR_UNSUPPORTED for d != 128, dtype != FA_BF16 or
+ * Errors: as fa_fwd (d = 64 or 128), plus FA_ERR_UNSUPPORTED for dtype != FA_BF16 or
  * N > 262144; FA_ERR_INVALID_ARG for a NULL mask or a stride that is neither 0
  * nor >= nb * nb.
  */
@@ -181,9 +181,9 @@ fa_status fa_bwd_stage(int stage, const void* q, const void* k, const void* v, c
  * causal additionally keeps j <= i). Deterministic: no atomics, every sum is
  * taken in a fixed order (the deterministic backward of the v2.4 changelog
  * entry, hysenlabs digest, constraints section, holds for every backward
- * here). Arguments, layouts, workspace and errors as fa_bwd, plus
- * FA_ERR_INVALID_ARG for a window side < -1 and FA_ERR_UNSUPPORTED for a
- * window with d != 128. With both sides -1 this is fa_bwd.
+ * here). Arguments, layouts, workspace and errors as fa_bwd (d = 64 or 128),
+ * plus FA_ERR_INVALID_ARG for a window side < -1. With both sides -1 this is
+ * fa_bwd.
  */
 fa_status fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, void* dq, void* dk, void* dv, void* workspace,

@@ -92,9 +92,9 @@ def test_window_validation(lib):
     bad = list(args)
     bad[12] = -2  # window_left
     assert lib.fa_fwd_window(*bad) == _lib.FA_ERR_INVALID_ARG
-    d64 = list(args)
-    d64[9] = 64
-    assert lib.fa_fwd_window(*d64) == _lib.FA_ERR_UNSUPPORTED
+    d96 = list(args)
+    d96[9] = 96  # d = 64 and 128 are the head dims built
+    assert lib.fa_fwd_window(*d96) == _lib.FA_ERR_UNSUPPORTED
     f32 = list(args)
     f32[14] = _lib.FA_FP32
     assert lib.fa_fwd_window(*f32) == _lib.FA_ERR_UNSUPPORTED
@@ -109,9 +109,9 @@ def test_bwd_window_validation(lib):
     bad = list(args)
     bad[18] = -3  # window_left
     assert lib.fa_bwd_window(*bad) == _lib.FA_ERR_INVALID_ARG
-    d64 = list(args)
-    d64[15] = 64
-    assert lib.fa_bwd_window(*d64) == _lib.FA_ERR_UNSUPPORTED
+    d96 = list(args)
+    d96[15] = 96
+    assert lib.fa_bwd_window(*d96) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_error().decode().startswith("fa_bwd_window")
 
 
@@ -119,7 +119,7 @@ def test_blocksparse_validation(lib):
     args = [FAKE] * 6 + [0, 1, 4, 2, 1000, 128, 0.1, 1, _lib.FA_BF16, None]
     for idx, val, status in ((5, None, _lib.FA_ERR_INVALID_ARG),      # block_mask
                              (6, 3, _lib.FA_ERR_INVALID_ARG),         # stride below nb*nb
-                             (11, 64, _lib.FA_ERR_UNSUPPORTED),       # d
+                             (11, 96, _lib.FA_ERR_UNSUPPORTED),       # d
                              (10, 300000, _lib.FA_ERR_UNSUPPORTED),   # N too large
                              (14, _lib.FA_FP32, _lib.FA_ERR_UNSUPPORTED)):
         bad = list(args)
@@ -136,7 +136,7 @@ def test_varlen_validation(lib):
                              (9, 0, _lib.FA_ERR_INVALID_ARG),       # total_q
                              (10, -1, _lib.FA_ERR_INVALID_ARG),     # total_k
                              (11, 3, _lib.FA_ERR_INVALID_ARG),      # Hq not a multiple of Hkv
-                             (13, 64, _lib.FA_ERR_UNSUPPORTED),     # d
+                             (13, 96, _lib.FA_ERR_UNSUPPORTED),     # d
                              (17, -5, _lib.FA_ERR_INVALID_ARG),     # window_right
                              (18, _lib.FA_FP32, _lib.FA_ERR_UNSUPPORTED),
                              (5, None, _lib.FA_ERR_INVALID_ARG),    # cu_seqlens_q

@@ -1,5 +1,5 @@
-"""GPU parity of fa_fwd_blocksparse (128 x 128 block mask, d = 128 bf16)
-against the fp64 oracle, through the C ABI."""
+"""GPU parity of fa_fwd_blocksparse (128 x 128 block mask, bf16, d = 128 and
+64) against the fp64 oracle, through the C ABI."""
 from __future__ import annotations
 
 import math
@@ -25,13 +25,14 @@ def _check(o, lse, ro, rl):
     assert_bf16_close(torch.from_numpy(g[fin]), w[fin], "LSE")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("per_head", [False, True])
-def test_random_mask(per_head, causal):
+def test_random_mask(per_head, causal, d):
     fa = need_gpu()
-    B, N, Hq, Hkv, d = 2, 700, 4, 2, 128
+    B, N, Hq, Hkv = 2, 700, 4, 2
     nb = (N + 127) // 128
-    announce(f"fwd blocksparse per_head={per_head} causal={causal}")
+    announce(f"fwd blocksparse per_head={per_head} causal={causal} d{d}")
     inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=60)
     rng = np.random.default_rng(61)
     mask = (rng.random((B, Hq, nb, nb) if per_head else (nb, nb)) < 0.45).astype(np.uint8)
@@ -43,10 +44,14 @@ def test_random_mask(per_head, causal):
     _check(o, lse, ro, rl)
 
 
-def test_all_ones_is_dense_bitwise_and_all_zeros_is_empty():
+# At d = 64 the dense batch must launch more than 256 workgroups of 128 rows
+# (2 x 16 heads x 8 tiles = 256 + 16 here) to run the same kernel as the
+# block-sparse path rather than the split-key one.
+@pytest.mark.parametrize("shape", [(1, 1000, 4, 1, 128), (2, 1000, 17, 1, 64)], ids=["d128", "d64"])
+def test_all_ones_is_dense_bitwise_and_all_zeros_is_empty(shape):
     fa = need_gpu()
-    announce("fwd blocksparse all-ones / all-zeros")
-    B, N, Hq, Hkv, d = 1, 1000, 4, 1, 128
+    B, N, Hq, Hkv, d = shape
+    announce(f"fwd blocksparse all-ones / all-zeros {shape}")
     nb = (N + 127) // 128
     inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=62)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))

@@ -1,5 +1,6 @@
 """GPU parity of the sliding-window and variable-length forwards (fa_fwd_window,
-fa_fwd_varlen, d = 128 bf16) against the fp64 oracle, through the C ABI."""
+fa_fwd_varlen, bf16, d = 128 and 64) and of the windowed backward against the
+fp64 oracle, through the C ABI."""
 from __future__ import annotations
 
 import math
@@ -28,12 +29,13 @@ def _check_lse(got, want, what):
 WINDOWS = [(0, 0), (1, 0), (64, 0), (100, 37), (-1, 5), (7, -1), (300, 300)]
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window", WINDOWS, ids=[f"w{a}_{b}" for a, b in WINDOWS])
-def test_window_dense(window, causal):
+def test_window_dense(window, causal, d):
     fa = need_gpu()
-    B, N, Hq, Hkv, d = 2, 333, 4, 2, 128
-    announce(f"fwd window {window} causal={causal} B{B} N{N}")
+    B, N, Hq, Hkv = 2, 333, 4, 2
+    announce(f"fwd window {window} causal={causal} B{B} N{N} d{d}")
     inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=31)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o, lse = fa.fa_fwd_window(q, k, v, window, causal=causal)
@@ -63,43 +65,49 @@ VARLEN_CASES = {
 }
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("name", sorted(VARLEN_CASES))
-def test_varlen(name, causal):
+def test_varlen(name, causal, d):
     fa = need_gpu()
     lens_q, lens_k = VARLEN_CASES[name]
-    announce(f"fwd varlen {name} causal={causal}")
-    inp = workloads.varlen_inputs(lens_q, lens_k, 4, 2, 128, seed=33)
+    announce(f"fwd varlen {name} causal={causal} d{d}")
+    inp = workloads.varlen_inputs(lens_q, lens_k, 4, 2, d, seed=33)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o, lse = fa.fa_fwd_varlen(q, k, v, inp["cu_q"].to(DEV), inp["cu_k"].to(DEV), max(lens_q), causal=causal)
     torch.cuda.synchronize()
     ro, rl = oracle.attn_fwd_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_q"].numpy(),
-                                    inp["cu_k"].numpy(), 1 / math.sqrt(128), causal)
+                                    inp["cu_k"].numpy(), 1 / math.sqrt(d), causal)
     assert_bf16_close(o.cpu(), ro, "O")
     _check_lse(lse.cpu(), rl, "LSE")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("window", [(16, 0), (50, 50), (0, -1)], ids=["w16_0", "w50_50", "w0_inf"])
-def test_varlen_window(window):
+def test_varlen_window(window, d):
     fa = need_gpu()
     lens_q, lens_k = [77, 300, 1, 129], [200, 300, 64, 129]
-    announce(f"fwd varlen window {window}")
-    inp = workloads.varlen_inputs(lens_q, lens_k, 8, 1, 128, seed=34)
+    announce(f"fwd varlen window {window} d{d}")
+    inp = workloads.varlen_inputs(lens_q, lens_k, 8, 1, d, seed=34)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     o, lse = fa.fa_fwd_varlen(q, k, v, inp["cu_q"].to(DEV), inp["cu_k"].to(DEV), max(lens_q), causal=True,
                               window=window)
     torch.cuda.synchronize()
     ro, rl = oracle.attn_fwd_varlen(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), inp["cu_q"].numpy(),
-                                    inp["cu_k"].numpy(), 1 / math.sqrt(128), True, window)
+                                    inp["cu_k"].numpy(), 1 / math.sqrt(d), True, window)
     assert_bf16_close(o.cpu(), ro, "O")
     _check_lse(lse.cpu(), rl, "LSE")
 
 
-def test_varlen_equal_lengths_matches_dense_bitwise():
+# d = 64 dense batches of at most 256 workgroups of 128 rows run the split-key
+# kernel, whose sums are ordered differently; 3 x 16 heads x 6 tiles = 288
+# workgroups run the same 128-row kernel as the packed batch.
+@pytest.mark.parametrize("shape", [(3, 320, 4, 2, 128), (3, 700, 16, 4, 64)], ids=["d128", "d64"])
+def test_varlen_equal_lengths_matches_dense_bitwise(shape):
     """Packing equal-length sequences is the dense batch: same kernel arithmetic, same bits."""
     fa = need_gpu()
-    announce("fwd varlen == dense")
-    B, N, Hq, Hkv, d = 3, 320, 4, 2, 128
+    B, N, Hq, Hkv, d = shape
+    announce(f"fwd varlen == dense {shape}")
     inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=35)
     q, k, v = (inp[n].to(DEV) for n in ("q", "k", "v"))
     cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=DEV)
@@ -126,13 +134,14 @@ def test_varlen_rows_past_max_seqlen_are_not_written():
     assert_bf16_close(o[:100 + 256].cpu(), ro[:100 + 256], "O of launched rows")
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("window", [(0, 0), (64, 0), (100, 37), (-1, 5), (7, -1), (200, 200)],
                          ids=["w0_0", "w64_0", "w100_37", "winf_5", "w7_inf", "w200_200"])
-def test_window_backward(window, causal):
+def test_window_backward(window, causal, d):
     fa = need_gpu()
-    B, N, Hq, Hkv, d = 1, 333, 4, 2, 128
-    announce(f"bwd window {window} causal={causal} N{N}")
+    B, N, Hq, Hkv = 1, 333, 4, 2
+    announce(f"bwd window {window} causal={causal} N{N} d{d}")
     inp = workloads.prefill_inputs(B, N, Hq, Hkv, d, "bf16", seed=37, with_do=True)
     q, k, v, do = (inp[n].to(DEV) for n in ("q", "k", "v", "do"))
     o, lse = fa.fa_fwd_window(q, k, v, window, causal=causal)
