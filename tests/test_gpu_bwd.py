@@ -22,6 +22,9 @@ SWEEP = [
     (1, 200, 4, 4, 64),
     (1, 257, 8, 2, 128),
     (1, 512, 2, 1, 128),
+    (2, 300, 6, 2, 128),     # 3 query heads per kv head
+    (4, 260, 12, 2, 128),    # 6 per kv head; B*Hkv = 8: dK/dV in XCD order
+    (1, 190, 5, 1, 64),      # 5 per kv head, d = 64
 ]
 
 

@@ -37,6 +37,9 @@ SMALL = [
     (2, 4, 4, 64, 1000, [999, 513]),
     (4, 32, 8, 128, 1500, [1500, 1024, 7, 640]),
     (2, 16, 1, 128, 700, [700, 65]),
+    (3, 24, 8, 128, 900, [900, 1, 333]),    # 3 query heads per kv head: one head per workgroup
+    (2, 10, 2, 64, 500, [500, 77]),         # 5 per kv head, d = 64
+    (2, 24, 2, 128, 700, [700, 300]),       # 12 per kv head: groups of 4
 ]
 
 
@@ -122,6 +125,8 @@ BALANCED = [
     (2, 8, 4, 128, 40000, [40000, 33]),                      # ranges far longer than a chunk
     (4, 8, 8, 128, 3000, [3000, 1, 2500, 17]),               # one query head per kv head
     (3, 64, 4, 128, 5000, [5000, 4096, 1]),                  # 16 query heads per kv head
+    (4, 24, 8, 128, 1200, [1200, 5, 640, 1199]),             # 3 query heads per kv head
+    (3, 20, 4, 64, 800, [800, 2, 513]),                      # 5 per kv head, d = 64
 ]
 
 

@@ -62,6 +62,10 @@ SWEEP = [
     (4, 1100, 16, 4, 64),    # d = 64 with 576 workgroups of 128 rows: the DMA kernel with 128-byte rows
     (2, 1500, 16, 2, 64),    # d = 64 DMA kernel: ragged last tile, 8 query heads per kv head
     (3, 900, 12, 3, 64),     # d = 64 DMA kernel: 288 workgroups, B = 3, 4 query heads per kv head
+    (2, 300, 6, 2, 128),     # 3 query heads per kv head (B*Hq = 12: plain block order)
+    (4, 260, 6, 2, 128),     # 3 per kv head, B*Hq = 24: XCD order with a partial head group (3 of 4)
+    (1, 190, 5, 1, 64),      # 5 query heads per kv head, d = 64 split-key kernel
+    (4, 1100, 12, 2, 64),    # 6 per kv head, d = 64 DMA kernel (432 workgroups, XCD order)
 ]
 
 
