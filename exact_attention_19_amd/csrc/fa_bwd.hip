@@ -565,6 +565,264 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_d128_ke
   }
 }
 
+// dK, dV at d = 128 (no window): one workgroup per (b, kv head, 128 keys) as
+// above, but with 8 waves so that two share each SIMD. Waves w and w + 4 (one
+// SIMD) take keys k0 + 32 (w % 4) .. +31 and query half w / 4 (rows 32 (w / 4)
+// .. +31) of every 64-query tile. K and V of the workgroup's 128 keys sit in
+// LDS and are read as MFMA operands like the Q and dO tiles, so a wave holds
+// only its dK^T, dV^T accumulators (128 registers) and one block's scores,
+// about 210 registers in all, where the four-wave kernel needs ~480 and runs
+// one wave per SIMD. The cost is one more 16-byte LDS read per S and dP MFMA;
+// in exchange the two waves of a SIMD hide each other's exponentials, LDS
+// latency and barrier waits. The tiles are visited in the same two phases,
+// each unrolled over the two ring stages. At the end the waves of query half
+// 1 pass their partial dK, dV to their partners through LDS.
+template <bool CAUSAL, bool WINDOW>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ lse2, const float* __restrict__ delta,
+    __bf16* __restrict__ dk, __bf16* __restrict__ dv, int B, int Hq, int Hkv, int N, float scale,
+    float scale_log2, int win_left, int win_right) {
+  constexpr int D = 128, DS = 8, DB = 4, BKV = 128, BQ = 64;
+  const int wl = WINDOW ? win_left : -1;
+  const int wr = WINDOW ? win_right : -1;
+  constexpr int ROWB = 2 * D;
+  constexpr int QBLK = 32 * ROWB;
+  constexpr int TILE = BQ * ROWB;
+  constexpr int VEC_OFF = 2 * TILE;
+  constexpr int STAGE = 2 * TILE + 8 * BQ;
+  constexpr int KT_OFF = 2 * STAGE;            // K rows k0 .. k0 + 127 (two 64-row tiles)
+  constexpr int VT_OFF = KT_OFF + 2 * TILE;    // V rows likewise
+  extern __shared__ __align__(1024) unsigned char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kb = wave & 3, qh = wave >> 2;
+  const int l32 = lane & 31, hh = lane >> 5;
+
+  const int BHK = B * Hkv;
+  const int nkt = (N + BKV - 1) / BKV;
+  int bhk, kt;
+  if (BHK % 8 == 0) {
+    xcd_order(blockIdx.x, BHK, nkt, kDkdvHeadGroup, bhk, kt);
+  } else {
+    bhk = blockIdx.x % BHK;
+    kt = blockIdx.x / BHK;
+  }
+  const int b = uniform(bhk / Hkv);
+  const int hk = uniform(bhk - b * Hkv);
+  const int G = Hq / Hkv;
+
+  const int64_t q_rs = (int64_t)Hq * D;
+  const int64_t kv_rs = (int64_t)Hkv * D;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + kb * 32;
+  const int my_key = kw0 + l32;
+  const bool wave_active = kw0 < N;
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int k_last = k0 + BKV - 1;
+  int q_lo_row = 0, q_hi_row = N - 1;  // queries that see some key of the workgroup
+  if (CAUSAL) q_lo_row = k0;
+  if (WINDOW && wr >= 0) q_lo_row = max(q_lo_row, k0 - wr);
+  if (WINDOW && wl >= 0) q_hi_row = min(q_hi_row, k_last + wl);
+  const int qlo = min(max(q_lo_row, 0), N) / BQ;
+  const int qhi = q_hi_row >= max(q_lo_row, 0) ? q_hi_row / BQ + 1 : qlo;
+  int f_lo = qlo, f_hi = qhi;
+  if (CAUSAL) f_lo = max(f_lo, (k_last + BQ - 1) / BQ);
+  if (WINDOW && wr >= 0) f_lo = max(f_lo, (max(k_last - wr, 0) + BQ - 1) / BQ);
+  if (WINDOW && wl >= 0) f_hi = min(f_hi, k0 + wl - (BQ - 1) >= 0 ? (k0 + wl - (BQ - 1)) / BQ + 1 : 0);
+  if (N % BQ != 0) f_hi = min(f_hi, nqt - 1);
+  f_lo = min(f_lo, qhi);
+  f_hi = max(f_hi, f_lo);
+  const int n_lo = f_lo - qlo;
+  const int n_m = n_lo + (qhi - f_hi);
+  const int n_u = f_hi - f_lo;
+  const int n1 = G * n_m;
+  const int n_iter = n1 + G * n_u;
+  struct Cursor { int h, j; };
+  auto tile_at = [&](int it, Cursor c, int& hq, int& q0) __attribute__((always_inline)) {
+    hq = hk * G + c.h;
+    if (it < n1) q0 = (c.j < n_lo ? qlo + c.j : f_hi + (c.j - n_lo)) * BQ;
+    else q0 = (f_lo + c.j) * BQ;
+  };
+  auto advance = [&](int it, Cursor c) __attribute__((always_inline)) {
+    if (it + 1 == n1) return Cursor{0, 0};
+    const int n = it < n1 ? n_m : n_u;
+    return c.j + 1 < n ? Cursor{c.h, c.j + 1} : Cursor{c.h + 1, 0};
+  };
+  Cursor cur{0, 0};
+
+  const int roff = row_offset<D>(lane);
+  int toff[2];
+  tr_offsets<D>(lane, toff);
+  const uint32_t q_rs_bytes = (uint32_t)(q_rs * 2);
+  const uint32_t kv_rs_bytes = (uint32_t)(kv_rs * 2);
+  const uint32_t dma_off = dma_lane_offset(lane, wave, q_rs_bytes);
+
+  f32x16 dkacc[DB], dvacc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) { dkacc[i] = f32x16{}; dvacc[i] = f32x16{}; }
+
+  // Q and dO tiles: 16 chunks of 1 KB each, two per wave; LSE2 and D by waves 0, 1.
+  auto issue = [&](int it, Cursor c, int stage) __attribute__((always_inline)) {
+    int hq, q0;
+    tile_at(it, c, hq, q0);
+    unsigned char* st = smem + stage * STAGE;
+    const int64_t off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
+    dma_rows64(reinterpret_cast<const unsigned char*>(q) + off, q_rs_bytes, N - q0, st, wave, 8, 2, dma_off);
+    dma_rows64(reinterpret_cast<const unsigned char*>(dout) + off, q_rs_bytes, N - q0, st + TILE, wave, 8, 2, dma_off);
+    const int64_t vb = ((int64_t)b * Hq + hq) * N;
+    if (wave == 0) dma_vec64_f32(lse2 + vb, q0, N - 1, st + VEC_OFF, lane);
+    if (wave == 1) dma_vec64_f32(delta + vb, q0, N - 1, st + VEC_OFF + 4 * BQ, lane);
+  };
+
+  struct Scores { f32x16 s, dp; };
+  struct Probs { bf16x8 p[2], ds[2]; };
+  const unsigned char* ks = smem + KT_OFF + kb * QBLK;
+  const unsigned char* vs = smem + VT_OFF + kb * QBLK;
+  auto scores = [&](const unsigned char* st) __attribute__((always_inline)) {
+    const unsigned char* qs = st + qh * QBLK;
+    const unsigned char* ds_ = st + TILE + qh * QBLK;
+    Scores r{f32x16{}, f32x16{}};
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const int o = roff ^ (32 * s);
+      r.s = mfma32(*reinterpret_cast<const bf16x8*>(qs + o), *reinterpret_cast<const bf16x8*>(ks + o), r.s);
+      r.dp = mfma32(*reinterpret_cast<const bf16x8*>(ds_ + o), *reinterpret_cast<const bf16x8*>(vs + o), r.dp);
+    }
+    return r;
+  };
+  auto apply_mask = [&](Scores& sc, int q0) __attribute__((always_inline)) {
+    const int qbase = q0 + 32 * qh + 4 * hh;
+    int lo = CAUSAL ? my_key - qbase : -1;                        // masked iff c(e) < lo
+    if (WINDOW && wr >= 0) lo = max(lo, my_key - wr - qbase);
+    int hi = N - 1 - qbase;                                       // masked iff c(e) > hi
+    if (WINDOW && wl >= 0) hi = min(hi, my_key + wl - qbase);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 8 * (e >> 2) + (e & 3);
+      sc.s[e] = (c < lo || c > hi) ? kNegInf : sc.s[e];
+    }
+  };
+  auto algebra = [&](const unsigned char* st, const Scores& sc) __attribute__((always_inline)) {
+    const float* lse_s = reinterpret_cast<const float*>(st + VEC_OFF);
+    const float* dlt_s = lse_s + BQ;
+    Probs r;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_s + 32 * qh + 8 * jj + 4 * hh);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(dlt_s + 32 * qh + 8 * jj + 4 * hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * jj + i;
+        const float p = fast_exp2(fmaf(sc.s[e], scale_log2, -l4[i]));
+        r.p[e >> 3][e & 7] = (__bf16)p;
+        r.ds[e >> 3][e & 7] = (__bf16)(p * (sc.dp[e] - d4[i]));
+      }
+    }
+    return r;
+  };
+  auto update = [&](const unsigned char* st, const Probs& pr) __attribute__((always_inline)) {
+    const unsigned char* qs = st;
+    const unsigned char* ds_ = st + TILE;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const int stp = 2 * qh + tt;
+        dvacc[db] = mfma32(tr_operand<D>(ds_, stp, db, toff), pr.p[tt], dvacc[db]);
+        dkacc[db] = mfma32(tr_operand<D>(qs, stp, db, toff), pr.ds[tt], dkacc[db]);
+      }
+    }
+  };
+  auto step = [&](int it, auto stage_tag, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int STG = decltype(stage_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const Cursor nxt = advance(it, cur);
+    if (it + 1 < n_iter) issue(it + 1, nxt, STG ^ 1);
+    int hq_cur, q0;
+    tile_at(it, cur, hq_cur, q0);
+    cur = nxt;
+    const int qw = q0 + 32 * qh;  // this wave's 32 queries
+    bool skip = !wave_active || (CAUSAL && qw + 31 < kw0);
+    if (WINDOW && wr >= 0) skip = skip || qw + 31 < kw0 - wr;
+    if (WINDOW && wl >= 0) skip = skip || qw > kw0 + 31 + wl;
+    if (!skip) {
+      const unsigned char* st = smem + STG * STAGE;
+      Scores sc = scores(st);
+      if constexpr (MASK) apply_mask(sc, q0);
+      const Probs p = algebra(st, sc);
+      update(st, p);
+    }
+    wait_vmcnt<0>();
+    barrier_keep_dma();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+
+  {
+    const unsigned char* kt0 = reinterpret_cast<const unsigned char*>(k) + ((int64_t)b * N + k0) * kv_rs * 2 +
+                               (int64_t)hk * D * 2;
+    const unsigned char* vt0 = reinterpret_cast<const unsigned char*>(v) + ((int64_t)b * N + k0) * kv_rs * 2 +
+                               (int64_t)hk * D * 2;
+    const uint32_t kdma_off = dma_lane_offset(lane, wave, kv_rs_bytes);
+    dma_rows64(kt0, kv_rs_bytes, N - k0, smem + KT_OFF, wave, 8, 2, kdma_off);
+    dma_rows64(kt0 + (int64_t)64 * kv_rs * 2, kv_rs_bytes, N - k0 - 64, smem + KT_OFF + TILE, wave, 8, 2, kdma_off);
+    dma_rows64(vt0, kv_rs_bytes, N - k0, smem + VT_OFF, wave, 8, 2, kdma_off);
+    dma_rows64(vt0 + (int64_t)64 * kv_rs * 2, kv_rs_bytes, N - k0 - 64, smem + VT_OFF + TILE, wave, 8, 2, kdma_off);
+  }
+  if (n_iter > 0) issue(0, cur, 0);
+  wait_vmcnt<0>();
+  barrier_keep_dma();
+  int it = 0;
+  for (; it + 1 < n1; it += 2) {
+    step(it, S0{}, std::true_type{});
+    step(it + 1, S1{}, std::true_type{});
+  }
+  if (it < n1) step(it++, S0{}, std::true_type{});
+  if (it < n_iter && (it & 1)) step(it++, S1{}, std::false_type{});
+  for (; it + 1 < n_iter; it += 2) {
+    step(it, S0{}, std::false_type{});
+    step(it + 1, S1{}, std::false_type{});
+  }
+  if (it < n_iter) step(it, S0{}, std::false_type{});
+
+  // Partial sums of the query halves: waves 4-7 hand theirs to waves 0-3
+  // through LDS (the ring and the K/V rows are no longer read: every wave has
+  // passed the last barrier), 512 bytes per lane, 16-byte pieces lane-major.
+  f32x4* red = reinterpret_cast<f32x4*>(smem) + (kb * 2 * DB * 4) * 64 + lane;
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        red[((0 * DB + db) * 4 + j) * 64] = f32x4{dkacc[db][4 * j], dkacc[db][4 * j + 1], dkacc[db][4 * j + 2], dkacc[db][4 * j + 3]};
+        red[((1 * DB + db) * 4 + j) * 64] = f32x4{dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]};
+      }
+    }
+  }
+  __syncthreads();
+  if (qh == 1 || !wave_active || my_key >= N) return;
+  const int64_t off = ((int64_t)b * N + my_key) * kv_rs + (int64_t)hk * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4 pk = red[((0 * DB + db) * 4 + j) * 64];
+      const f32x4 pv = red[((1 * DB + db) * 4 + j) * 64];
+      const int d = db * 32 + 8 * j + 4 * hh;
+      u32x2 wk, wv;
+      wk[0] = pack_bf16x2((dkacc[db][4 * j + 0] + pk[0]) * scale, (dkacc[db][4 * j + 1] + pk[1]) * scale);
+      wk[1] = pack_bf16x2((dkacc[db][4 * j + 2] + pk[2]) * scale, (dkacc[db][4 * j + 3] + pk[3]) * scale);
+      wv[0] = pack_bf16x2(dvacc[db][4 * j + 0] + pv[0], dvacc[db][4 * j + 1] + pv[1]);
+      wv[1] = pack_bf16x2(dvacc[db][4 * j + 2] + pv[2], dvacc[db][4 * j + 3] + pv[3]);
+      *reinterpret_cast<u32x2*>(dk + off + d) = wk;
+      *reinterpret_cast<u32x2*>(dv + off + d) = wv;
+    }
+  }
+}
+
 // dQ (d = 128 or 64): one workgroup per (b, query head, 128 query rows),
 // shaped like the forward: S^T = K Q^T, dP^T = V dO^T, dQ^T += K^T dS^T.
 template <bool CAUSAL, bool WINDOW, int D = 128>
@@ -851,7 +1109,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
         return hipGetLastError();
       }
     }
-    {
+    if constexpr (D == 128) {
+      auto kern = bwd_dkdv8_kernel<CAUSAL, WINDOW>;
+      constexpr size_t smem = 2 * (2 * 64 * 256 + 8 * 64) + 2 * 2 * 64 * 256;  // Q/dO ring + K, V rows
+      hipError_t e = set_smem_once<bwd_dkdv8_kernel<CAUSAL, WINDOW>>(smem);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), smem, a.stream, (const __bf16*)a.q,
+                         (const __bf16*)a.k, (const __bf16*)a.v, (const __bf16*)a.dout, (const float*)lse2,
+                         (const float*)delta, (__bf16*)a.dk, (__bf16*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.scale,
+                         scale_log2, a.win_left, a.win_right);
+      return hipGetLastError();
+    } else {
       constexpr int BQ = kDkdvQueryTile;
       auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ, false, D>;
       constexpr size_t smem = 2 * (2 * BQ * 2 * D + 8 * BQ) + (D == 128 && !WINDOW ? 256 : 0);  // + dump slot

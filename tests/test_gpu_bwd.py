@@ -96,8 +96,10 @@ ATOMIC = [
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", ATOMIC, ids=[f"B{b}N{n}Hq{hq}Hkv{hk}d{d}" for b, n, hq, hk, d in ATOMIC])
 def test_bwd_atomic(shape, causal):
-    """fa_bwd_atomic: dQ, dK, dV against the oracle; dK and dV bitwise equal
-    to the deterministic backward's; every output written (NaN-filled)."""
+    """fa_bwd_atomic: dQ, dK, dV against the oracle; dK and dV within one bf16
+    ulp of the deterministic backward's (the same fp32 terms, summed in
+    another order: the deterministic d = 128 kernel adds the two query halves
+    of every tile in separate waves); every output written (NaN-filled)."""
     fa = need_gpu()
     B, N, Hq, Hkv, d = shape
     announce(f"bwd atomic {shape} causal={causal}")
@@ -109,7 +111,13 @@ def test_bwd_atomic(shape, causal):
     fa.fa_bwd(q, k, v, o, do, lse, causal=causal, dq=dq, dk=dk, dv=dv, deterministic=False)
     rq, rk, rv = fa.fa_bwd(q, k, v, o, do, lse, causal=causal)
     torch.cuda.synchronize()
-    assert torch.equal(dk, rk) and torch.equal(dv, rv)
+    for name, x, y in (("dK", dk, rk), ("dV", dv, rv)):
+        x64, y64 = x.double(), y.double()
+        big = torch.maximum(x64.abs(), y64.abs())
+        ulp = torch.ldexp(torch.ones_like(big), torch.frexp(big).exponent - 8)
+        gap = (x64 - y64).abs()
+        assert torch.isfinite(x64).all() and bool((gap <= ulp + 1e-6).all()), \
+            f"{name}: atomic and deterministic differ by {float((gap - ulp).max()):.3e} beyond one ulp"
     rdq, rdk, rdv, _ = oracle.attn_bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["do"]),
                                        1 / math.sqrt(d), causal)
     assert_bf16_close(dq, rdq, "dQ")
