@@ -137,11 +137,13 @@ __device__ __forceinline__ int row_offset(int lane) {
   return l32 * 2 * D + 16 * (hh ^ row_swz<D>(l32));
 }
 
-// dK, dV (d = 128 or 64): one workgroup per (b, kv head, 128 keys); wave w keeps
+// dK, dV, four waves: one workgroup per (b, kv head, 128 keys); wave w keeps
 // keys k0 + 32w .. +31 (K, V fragments and dK^T, dV^T accumulators in
 // registers) and sweeps the visible 64-row query tiles of every query head
-// in the GQA group. At d = 64 the fragments and accumulators take half the
-// registers (248 in all), so two workgroups share a CU; at d = 128 one does.
+// in the GQA group. Launched for d = 64, where the fragments and
+// accumulators take half the registers (248 in all) so two workgroups share
+// a CU, and for the fused dQ below at d = 128 (one wave per SIMD); the
+// deterministic d = 128 backward runs bwd_dkdv8_kernel.
 //
 // FUSED (the atomic backward) also produces dQ, so that the backward runs
 // the five N x N x d products once each instead of recomputing S and dP in a
@@ -284,46 +286,6 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_d128_ke
     }
   };
 
-  // d = 128: the next tile's DMA is spread over the tile body instead of
-  // issued in one burst at the top of the step (the memory pipe accepts about
-  // one 1 KB LDS-DMA instruction per 16 cycles, so a burst of the four waves'
-  // 32 instructions holds each wave for most of it). In parts, each issued at
-  // a hook of the body: the two halves of the wave's Q chunks after the first
-  // block's scores (hook 1), dO's halves before the two dV/dK updates (hooks 2
-  // and 3), LSE*log2(e) and D with the second (hook 3). Branch-free: on the
-  // last step the parts load nothing (a zero-length buffer range still writes
-  // zeros, into the unused stage), and waves 2-3, which have no LSE/D part,
-  // write their zeros to a slot past the ring. (Not with a window: the
-  // window bounds' extra scalar state then spills to scratch.)
-  constexpr bool SPREAD = D == 128 && !FUSED && !WINDOW;
-  constexpr int DUMP_OFF = 2 * STAGE;          // 256 bytes past the ring (SPREAD only)
-  constexpr int kHookOf[5] = {1, 1, 2, 3, 3};  // Q half 0, Q half 1, dO half 0, dO half 1, LSE/D
-  struct NextTile { int64_t off, vb; int nrows, q0; };
-  auto next_tile = [&](int it, Cursor c, bool live) __attribute__((always_inline)) {
-    int hq, q0;
-    tile_at(it, c, hq, q0);
-    NextTile t;
-    t.off = ((int64_t)b * N + q0) * q_rs * 2 + (int64_t)hq * D * 2;
-    t.vb = ((int64_t)b * Hq + hq) * N;
-    t.nrows = live ? N - q0 : 0;
-    t.q0 = q0;
-    return t;
-  };
-  auto issue_part = [&](const NextTile& t, int stage, int part) __attribute__((always_inline)) {
-    unsigned char* st = smem + stage * STAGE;
-    if (part < 4) {
-      const int tl = part >> 1, hf = part & 1;  // tile (Q, dO), half of the wave's chunks
-      const unsigned char* src = reinterpret_cast<const unsigned char*>(tl == 0 ? q : dout) + t.off;
-      dma_rows64_asm<D>(src, q_rs_bytes, t.nrows, st + tl * TILE, wave + 4 * (CPW / 2) * hf, 4, CPW / 2, dma_off);
-    } else {
-      const float* src = (wave == 0 ? lse2 : delta) + t.vb;
-      const uint32_t bytes = (t.nrows > 0 && wave < 2) ? 4u * (uint32_t)N : 0u;
-      const uint32_t idx = (uint32_t)min(t.q0 + lane, N - 1);
-      unsigned char* dst = wave < 2 ? st + VEC_OFF + 4 * BQ * wave : smem + DUMP_OFF;
-      lds_dma4(rsrc_words(src, bytes), 4u * idx, lds_addr(dst));
-    }
-  };
-
   // The tile's two 32-query blocks are skewed so that independent work sits
   // side by side for the scheduler: S/dP of block 1 next to the softmax
   // algebra of block 0, and the dV/dK products of block 0 next to the
@@ -451,24 +413,21 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_d128_ke
   // diagonal and the ragged end) run a branch-free body, one scheduling
   // region. (Pinning its issue order as in the dQ kernel measured slower
   // here, with one wave per SIMD; the compiler's order is kept.)
-  auto tile_body = [&](const unsigned char* st, int q0, auto mask_tag, unsigned char* dsb, auto hook)
+  auto tile_body = [&](const unsigned char* st, int q0, auto mask_tag, unsigned char* dsb)
                        __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     // Skewed over the NQB blocks: the scores of block qb + 1 are issued
     // before the algebra and products of block qb.
-    hook(0);
     Scores sa = scores(st, 0);
     if constexpr (MASK) apply_mask(sa, q0, 0);
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       Scores sb;
-      if (qb == 0) hook(1);
       if (qb + 1 < NQB) sb = scores(st, qb + 1);
       const Probs p = algebra(st, qb, sa);
       if (qb + 1 < NQB) {
         if constexpr (MASK) apply_mask(sb, q0, qb + 1);
       }
-      hook(qb == 0 ? 2 : 3);
       update(st, qb, p);
       if constexpr (FUSED) store_ds(dsb, qb, p);
       if (qb + 1 < NQB) sa = sb;
@@ -484,32 +443,14 @@ __global__ __launch_bounds__(kBwdThreads, D == 64 ? 2 : 1) void bwd_dkdv_d128_ke
     if constexpr (FUSED) {
       if (it > 0) dq_pass(smem + DSB_OFF + (STG ^ 1) * 16384, prev_hq, prev_q0, prev_skip);
     }
-    const bool more = it + 1 < n_iter;
-    if constexpr (!SPREAD) {
-      if (more) issue(it + 1, nxt, STG ^ 1);
-    }
+    if (it + 1 < n_iter) issue(it + 1, nxt, STG ^ 1);
     int hq_cur, q0;
     tile_at(it, cur, hq_cur, q0);
     cur = nxt;
     bool skip = !wave_active || (CAUSAL && q0 + BQ - 1 < kw0);
     if (WINDOW && wr >= 0) skip = skip || q0 + BQ - 1 < kw0 - wr;
     if (WINDOW && wl >= 0) skip = skip || q0 > kw0 + 31 + wl;
-    if constexpr (SPREAD) {
-      const NextTile nt = next_tile(it + 1, nxt, more);
-      if (skip) {
-#pragma unroll
-        for (int part = 0; part < 5; ++part) issue_part(nt, STG ^ 1, part);
-      } else {
-        auto hook = [&](int h) __attribute__((always_inline)) {
-#pragma unroll
-          for (int part = 0; part < 5; ++part)
-            if (h == kHookOf[part]) issue_part(nt, STG ^ 1, part);
-        };
-        tile_body(smem + STG * STAGE, q0, mask_tag, smem + DSB_OFF + STG * 16384, hook);
-      }
-    } else {
-      if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag, smem + DSB_OFF + STG * 16384, [](int) {});
-    }
+    if (!skip) tile_body(smem + STG * STAGE, q0, mask_tag, smem + DSB_OFF + STG * 16384);
     if constexpr (FUSED) {
       prev_hq = hq_cur;
       prev_q0 = q0;
@@ -1122,7 +1063,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, float* delta, int stage) {
     } else {
       constexpr int BQ = kDkdvQueryTile;
       auto kern = bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ, false, D>;
-      constexpr size_t smem = 2 * (2 * BQ * 2 * D + 8 * BQ) + (D == 128 && !WINDOW ? 256 : 0);  // + dump slot
+      constexpr size_t smem = 2 * (2 * BQ * 2 * D + 8 * BQ);
       hipError_t e = set_smem_once<bwd_dkdv_d128_kernel<CAUSAL, WINDOW, BQ, false, D>>(smem);
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBwdThreads), smem, a.stream, (const __bf16*)a.q,

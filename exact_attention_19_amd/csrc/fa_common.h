@@ -275,54 +275,6 @@ __device__ __forceinline__ void dma_rows64_d(const unsigned char* tile_base, uin
   }
 }
 
-// The same tile DMA written as inline assembly, for DMAs issued in the middle
-// of a loop body. The compiler does not track these loads: it cannot prove
-// that a ds_read_b64_tr_b16 of the tile being computed does not alias a
-// builtin DMA into the other stage, so after a builtin DMA it waits for the
-// DMA to land before the next transposed read; after these it does not, and
-// the caller waits for them itself (s_waitcnt vmcnt(0) before the barrier
-// that hands the stage over). Vector-memory loads complete in order, so the
-// compiler's own vmcnt waits stay correct (only more conservative). The
-// buffer resource is the same as make_rsrc's; M0 holds the LDS destination.
-__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xffffu;  // stride 0
-  r[2] = __builtin_amdgcn_readfirstlane(bytes);
-  r[3] = 0x00020000u;
-  return r;
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)p);
-}
-// 16 bytes per lane to LDS byte lds + 16 * lane.
-__device__ __forceinline__ void lds_dma16(u32x4 rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
-}
-// 4 bytes per lane to LDS byte lds + 4 * lane.
-__device__ __forceinline__ void lds_dma4(u32x4 rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
-               : : "v"(voff), "s"(rsrc), "s"(lds) : "memory", "m0");
-}
-// dma_rows64_d with the untracked loads (same chunks, same layout).
-template <int D>
-__device__ __forceinline__ void dma_rows64_asm(const unsigned char* tile_base, uint32_t stride_bytes, int nrows,
-                                               unsigned char* lds_tile, int first, int step, int nchunk,
-                                               uint32_t lane_off) {
-  constexpr int RPC = 1024 / (2 * D);
-  const uint32_t rows = (uint32_t)uniform(min(max(nrows, 0), 64));
-  const u32x4 r = rsrc_words(uniform(tile_base), rows * stride_bytes);
-  const uint32_t chunk_stride = (uint32_t)(RPC * step) * stride_bytes;
-  const uint32_t first_off = lane_off + (uint32_t)(RPC * first) * stride_bytes;
-#pragma unroll
-  for (int i = 0; i < nchunk; ++i) {
-    const int c = first + step * i;
-    lds_dma16(r, first_off + i * chunk_stride, lds_addr(lds_tile + c * 1024));
-  }
-}
-
 // DMA 64 consecutive floats src[i0 + lane] (indices clamped to `last`) into
 // LDS dst[lane]: one wave instruction.
 __device__ __forceinline__ void dma_vec64_f32(const float* src, int i0, int last, unsigned char* lds_dst, int lane) {
