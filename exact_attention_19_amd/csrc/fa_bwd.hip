@@ -694,7 +694,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       Scores sc = scores(st);
       if constexpr (MASK) apply_mask(sc, q0);
       const Probs p = algebra(st, sc);
+      // Issue priority while the wave feeds its dV/dK products: when both
+      // waves of the SIMD are ready, the one holding the matrix pipe keeps it
+      // (measured 0.5 % faster, bitwise equal).
+      __builtin_amdgcn_s_setprio(1);
       update(st, p);
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vmcnt<0>();
     barrier_keep_dma();
