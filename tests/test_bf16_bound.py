@@ -44,6 +44,16 @@ def test_many_heads_rounding_alone_meets_the_bound(shape, causal):
     assert all(r[2] <= 0 and r[1] <= 2e-3 for r in rep.values()), {k: v[:3] for k, v in rep.items()}
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", bwd_rounding.ODD_GROUPS)
+def test_odd_group_sweep_rounding_alone_meets_the_bound(shape, causal):
+    """The backward sweep cases with 3, 6 and 5 query heads per kv head, on
+    the sweep's own inputs (N(0,1)): rounding P and dS alone stays inside the
+    bound, so the GPU sweep can hold the kernels to it at full input scale."""
+    rep = bwd_rounding.emulation_report(shape, causal, seed=bwd_rounding.sweep_seed(shape))
+    assert all(r[2] <= 0 and r[1] <= 2e-3 for r in rep.values()), {k: v[:3] for k, v in rep.items()}
+
+
 def test_allowance_only_from_8_would_be_unattainable():
     """Why the output-rounding allowance applies at every magnitude: with it
     only where half an ulp exceeds 2e-2 (|x| >= 8), rounding P and dS alone
